@@ -1,0 +1,38 @@
+"""CPU fp64 oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY. The attention library never imports, calls or links
+anything in this package; only the test suite, the smoke check and the bench's
+CPU-baseline leg use it. It shares no code with the HIP path.
+
+* ``attention``: the plain definition, softmax(scale * q k^T) v, with the full
+  score matrix materialised in float64, its row logsumexp, and the gradients
+  obtained from the calculus of that definition.
+* ``online``: the tiled online-softmax recurrence in its two published forms
+  (normalise every block; defer the normalisation to the end), in float64,
+  written from the pages' description. It exists to check that tiling reaches
+  the same result as the definition.
+
+Parity status: every function here is pinned by tests under ``-m "not gpu"``
+against closed forms, hand-derived worked examples, identities, brute-force
+finite differences and a library routine (torch CPU float64).
+"""
+from .attention import (
+    attention_fwd,
+    attention_fwd_rows,
+    attention_probs,
+    attention_bwd,
+    attention_bwd_head,
+    causal_tile_count,
+)
+from .online import online_fwd_normalise_each_block, online_fwd_deferred
+
+__all__ = [
+    "attention_fwd",
+    "attention_fwd_rows",
+    "attention_probs",
+    "attention_bwd",
+    "attention_bwd_head",
+    "causal_tile_count",
+    "online_fwd_normalise_each_block",
+    "online_fwd_deferred",
+]
