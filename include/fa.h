@@ -1,0 +1,99 @@
+/*
+ * libfa: exact attention O = softmax(scale * Q K^T) V for AMD MI355X (gfx950),
+ * computed tile by tile with an online softmax so that the N x N score matrix
+ * never reaches device memory.
+ *
+ * The operation is the attention formula of the page "FlashAttention v2相比于v1
+ * 有哪些更新" (blogweb.cn), section 1; the tiling and the running max/sum
+ * recurrence are those of "FlashAttention技术解析：优化Transformer注意力机制"
+ * (mhpq.cn), sections 2.1-2.2, with the normalisation deferred to the end of
+ * the key loop as in the blogweb.cn page, section 3 ("Rescale操作"). The
+ * backward pass recomputes the probabilities from the stored row logsumexp,
+ * which is the "store only the softmax normalisation factor" strategy of the
+ * page "4.3 FlashAttention-2与FlashAttention-3演进", FlashAttention-3
+ * section 3 ("反向传播优化").
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  Layout    q, o, dout, dq : contiguous [B, Hq, N, d]   (row-major, d fastest)
+ *            k, v, dk, dv   : contiguous [B, Hkv, N, d]
+ *            lse            : contiguous [B, Hq, N] float32
+ *  Heads     query head h reads key/value head h / (Hq / Hkv) (grouped heads;
+ *            Hkv == Hq is ordinary multi-head attention).
+ *  Mask      causal != 0: key j is visible to query i iff j <= i.
+ *  Scale     applied to q.k before the softmax (usually 1/sqrt(d)).
+ *  lse       natural-log logsumexp of the scaled, masked scores of each query
+ *            row: lse_i = log(sum_j exp(scale * q_i.k_j)).
+ *  Memory    every pointer is a device pointer owned by the caller; the
+ *            library never allocates, frees or keeps a pointer past the call.
+ *            Base pointers must be 16-byte aligned.
+ *  Streams   work is enqueued on `stream` (NULL = the default stream) and the
+ *            call returns without synchronising; a device-side fault shows at
+ *            the caller's next synchronisation.
+ *  Empty     B == 0 or N == 0 is a valid empty problem: FA_OK, nothing is
+ *            touched (pointers may then be NULL).
+ *  Errors    a status code is returned; nothing is printed and nothing aborts.
+ *            Argument checks run before any HIP call, so FA_ERR_INVALID_ARG and
+ *            FA_ERR_UNSUPPORTED (shape) never depend on a device being present.
+ *  Threads   the library keeps no state besides a per-device architecture
+ *            check cached on first use; calls from several host threads are
+ *            safe.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative or inconsistent sizes, bad flag */
+  FA_ERR_UNSUPPORTED = -2, /* head dim not supported, or device is not gfx950 */
+  FA_ERR_DEVICE = -3,      /* no usable HIP device / device query failed */
+  FA_ERR_LAUNCH = -4,      /* a kernel launch reported an error */
+  FA_ERR_INTERNAL = -5
+} fa_status;
+
+/* Forward, bf16 storage (q, k, v, o as bf16 bit patterns), float32 arithmetic
+ * for the softmax and the accumulators, float32 lse. o is rounded to bf16
+ * round-to-nearest-even. Supported d: 64, 128. Sizes: B >= 0, N >= 0,
+ * Hq >= 1, Hkv >= 1, Hq % Hkv == 0, B*Hq*N*d < 2^31 elements per tensor. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/* Forward, float32 storage and float32 arithmetic throughout (no bf16
+ * rounding anywhere). Same arguments, layouts and limits as fa_fwd. */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (0 on invalid sizes). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/* Backward, bf16 storage. q, k, v are the forward inputs; o and lse are the
+ * forward outputs (fa_fwd); dout = dL/dO. Writes dq, dk, dv (bf16, RNE) =
+ * dL/dq, dL/dk, dL/dv. The probabilities are recomputed from lse. For grouped
+ * heads dk and dv sum over the query heads that read each key/value head.
+ * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
+ * 16-byte aligned, contents ignored on entry (float32 scratch for the row
+ * term D_i = sum_c dout_ic o_ic and the float32 dq accumulator).
+ * Supported d: 64, 128. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

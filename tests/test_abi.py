@@ -1,0 +1,97 @@
+"""The C ABI: library loads, exports what include/fa.h declares, and rejects bad
+arguments before touching HIP (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _lib():
+    from tiled_online_softmax_fa_amd import LIB_PATH, load_library
+
+    if not os.path.exists(LIB_PATH):
+        pytest.skip("libfa.so not built (run __graft_entry__.build())")
+    return load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_f32", "fa_status_string"]
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+BAD = ctypes.c_void_p(16)  # never dereferenced: validation fails before any use
+NULL = ctypes.c_void_p(0)
+
+
+def _fwd(lib, B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125, ptrs=None, entry="fa_fwd"):
+    p = ptrs or [BAD] * 5
+    return getattr(lib, entry)(*p, B, Hq, Hkv, N, d, causal, scale, NULL)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_forward_argument_errors(entry):
+    from tiled_online_softmax_fa_amd import FA_ERR_INVALID_ARG as INV, FA_ERR_UNSUPPORTED as UNS, FA_OK
+
+    lib = _lib()
+    assert _fwd(lib, d=96, entry=entry) == UNS
+    assert _fwd(lib, d=256, entry=entry) == UNS
+    assert _fwd(lib, Hq=3, Hkv=2, entry=entry) == INV
+    assert _fwd(lib, Hkv=0, entry=entry) == INV
+    assert _fwd(lib, B=-1, entry=entry) == INV
+    assert _fwd(lib, N=-5, entry=entry) == INV
+    assert _fwd(lib, causal=2, entry=entry) == INV
+    assert _fwd(lib, scale=float("nan"), entry=entry) == INV
+    assert _fwd(lib, scale=float("inf"), entry=entry) == INV
+    assert _fwd(lib, scale=0.0, entry=entry) == INV
+    assert _fwd(lib, scale=-0.5, entry=entry) == INV
+    assert _fwd(lib, B=1 << 12, Hq=64, Hkv=8, N=1 << 12, d=128, entry=entry) == INV  # >= 2^31 elements
+    assert _fwd(lib, ptrs=[BAD, BAD, NULL, BAD, BAD], entry=entry) == INV
+    misaligned = ctypes.c_void_p(16 + 2)
+    assert _fwd(lib, ptrs=[BAD, misaligned, BAD, BAD, BAD], entry=entry) == INV
+    # empty problems succeed without touching the pointers
+    assert _fwd(lib, B=0, ptrs=[NULL] * 5, entry=entry) == FA_OK
+    assert _fwd(lib, N=0, ptrs=[NULL] * 5, entry=entry) == FA_OK
+
+
+def test_backward_argument_errors():
+    from tiled_online_softmax_fa_amd import FA_ERR_INVALID_ARG as INV, FA_ERR_UNSUPPORTED as UNS, FA_OK
+
+    lib = _lib()
+    ws = lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 64)
+    assert ws >= 2 * 8 * 4 + 2 * 8 * 64 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 3, 2, 8, 64) == 0
+
+    def call(ptrs=None, wsb=ws, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125)
+        a.update(kw)
+        p = ptrs or [BAD] * 10
+        return lib.fa_bwd(*p, wsb, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], NULL)
+
+    assert call(d=80) == UNS
+    assert call(Hq=4, Hkv=3) == INV
+    assert call(wsb=ws - 1) == INV
+    assert call(ptrs=[BAD] * 9 + [NULL]) == INV
+    assert call(scale=-1.0) == INV
+    assert call(B=0, ptrs=[NULL] * 10, wsb=0) == FA_OK
+
+
+def test_status_strings():
+    lib = _lib()
+    for s in range(-6, 1):
+        assert lib.fa_status_string(s)

@@ -1,0 +1,203 @@
+"""Forward parity: libfa on the GPU against the fp64 CPU oracle, same seeded inputs."""
+import sys
+
+import numpy as np
+import pytest
+
+from fa_inputs import WORKLOADS, make_workload_inputs
+from fa_testlib import (F32_MAX_ABS, LSE_MAX_ABS, assert_bf16_close, errors, run_fwd, to_device, to_f64,
+                        torch_mod)
+from oracle import attention_fwd, attention_fwd_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d, causal  -- several tiles, ragged tails, grouped heads
+    (1, 2, 2, 300, 64, False),
+    (1, 2, 2, 300, 64, True),
+    (1, 2, 2, 300, 128, False),
+    (1, 2, 2, 300, 128, True),
+    (2, 8, 2, 513, 128, True),
+    (1, 4, 1, 1000, 64, True),
+    (1, 3, 3, 640, 128, False),
+    (2, 2, 1, 257, 64, False),
+    (1, 2, 2, 255, 128, True),
+    (1, 1, 1, 1, 64, False),
+    (1, 1, 1, 1, 128, True),
+    (1, 2, 2, 17, 128, True),
+    (1, 2, 2, 64, 64, True),
+    (1, 1, 1, 2048, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", SMALL)
+def test_fwd_bf16_small(B, Hq, Hkv, N, d, causal):
+    _say(f"fwd bf16 B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    inp, o, lse, scale = run_fwd(B, Hq, Hkv, N, d, causal, "bf16", seed=N + d)
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    mx, mean = assert_bf16_close(o, O, "O")
+    lmx, _ = errors(lse, LSE)
+    _say(f"  O max {mx:.2e} mean {mean:.2e}  lse max {lmx:.2e}")
+    assert lmx <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_bf16_peaky_scores(causal, d):
+    # q scaled by 8: softmax rows are dominated by a few keys and the running
+    # maximum moves often, exercising the rescale path
+    _say(f"fwd bf16 peaky d{d} causal={causal}")
+    inp, o, lse, scale = run_fwd(1, 4, 2, 700, d, causal, "bf16", seed=11, q_mult=8.0)
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    assert_bf16_close(o, O, "O")
+    assert errors(lse, LSE)[0] <= LSE_MAX_ABS * 8
+
+
+def test_fwd_bf16_increasing_keys_force_rescales():
+    # keys whose scores grow along the sequence: the reference maximum must move
+    # on nearly every tile
+    torch = torch_mod()
+    import tiled_online_softmax_fa_amd as fa
+    from fa_inputs import bf16_round_bits, bf16_bits_to_f32
+
+    N, d = 777, 128
+    rng = np.random.default_rng(5)
+    q = np.ones((1, 1, N, d), np.float32)
+    k = (np.linspace(0, 6, N, dtype=np.float32)[None, None, :, None] * np.ones((1, 1, 1, d), np.float32))
+    v = rng.standard_normal((1, 1, N, d), dtype=np.float32)
+    inp = {}
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        inp[n + "_bits"] = bf16_round_bits(x)
+        inp[n] = bf16_bits_to_f32(inp[n + "_bits"])
+    for causal in (False, True):
+        o, lse = fa.fwd(*(to_device(inp, n, "bf16") for n in ("q", "k", "v")), causal=causal, scale=0.05)
+        torch.cuda.synchronize()
+        O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, 0.05)
+        assert_bf16_close(to_f64(o), O, f"O causal={causal}")
+        assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS * 10
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 1, 1, 256, 64, False), (1, 2, 2, 300, 64, True),
+                                                 (2, 2, 1, 77, 128, False), (1, 1, 1, 1, 64, True)])
+def test_fwd_f32_small(B, Hq, Hkv, N, d, causal):
+    _say(f"fwd f32 B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    inp, o, lse, scale = run_fwd(B, Hq, Hkv, N, d, causal, "f32", seed=N)
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    mx, _ = errors(o, O)
+    lmx, _ = errors(lse, LSE)
+    _say(f"  O max {mx:.2e} lse max {lmx:.2e}")
+    assert np.isfinite(o).all() and mx <= F32_MAX_ABS and lmx <= F32_MAX_ABS
+
+
+def test_fwd_f32_workload_single_head_256():
+    w = WORKLOADS["fwd_f32_b1h1n256d64"]
+    _say(f"workload {w.name}")
+    inp = make_workload_inputs(w)
+    import tiled_online_softmax_fa_amd as fa
+
+    o, lse = fa.fwd_f32(*(to_device(inp, n, "f32") for n in ("q", "k", "v")), causal=w.causal, scale=w.scale)
+    torch_mod().cuda.synchronize()
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
+    mx, _ = errors(to_f64(o), O)
+    lmx, _ = errors(to_f64(lse), LSE)
+    _say(f"  O max {mx:.2e} lse max {lmx:.2e}")
+    assert mx <= F32_MAX_ABS and lmx <= F32_MAX_ABS
+
+
+def test_fwd_bf16_workload_multihead_2048_full():
+    w = WORKLOADS["fwd_bf16_b4h16n2048d64"]
+    _say(f"workload {w.name} (full oracle)")
+    inp = make_workload_inputs(w)
+    import tiled_online_softmax_fa_amd as fa
+
+    o, lse = fa.fwd(*(to_device(inp, n, "bf16") for n in ("q", "k", "v")), causal=w.causal, scale=w.scale)
+    torch_mod().cuda.synchronize()
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
+    mx, mean = assert_bf16_close(to_f64(o), O, "O")
+    _say(f"  O max {mx:.2e} mean {mean:.2e}")
+    assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
+
+
+def _sampled_check(w, n_full_heads=2, rows_per_head=48, seed=123):
+    """Full-size workload: every head checked on sampled rows, a few heads in full."""
+    import tiled_online_softmax_fa_amd as fa
+
+    inp = make_workload_inputs(w)
+    o, lse = fa.fwd(*(to_device(inp, n, "bf16") for n in ("q", "k", "v")), causal=w.causal, scale=w.scale)
+    torch_mod().cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            rows = np.unique(np.concatenate([[0, 1, w.N - 1], rng.integers(0, w.N, rows_per_head)]))
+            Or, Lr = attention_fwd_rows(inp["q"], inp["k"], inp["v"], w.causal, w.scale, b, h, rows)
+            mx, _ = errors(o[b, h, rows], Or)
+            worst = max(worst, mx)
+            assert mx <= 2e-2, f"head ({b},{h}) sampled rows: max {mx:.3e}"
+            assert errors(lse[b, h, rows], Lr)[0] <= LSE_MAX_ABS
+    G = w.Hq // w.Hkv
+    for i in range(n_full_heads):
+        b, h = i % w.B, (7 * i + 3) % w.Hq
+        O, LSE = attention_fwd(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h // G:h // G + 1],
+                               inp["v"][b:b + 1, h // G:h // G + 1], w.causal, w.scale)
+        assert_bf16_close(o[b:b + 1, h:h + 1], O, f"full head ({b},{h})")
+        assert errors(lse[b:b + 1, h:h + 1], LSE)[0] <= LSE_MAX_ABS
+    _say(f"  sampled worst max {worst:.2e}")
+
+
+def test_fwd_bf16_workload_causal_4096():
+    w = WORKLOADS["fwd_causal_bf16_b2h16n4096d128"]
+    _say(f"workload {w.name} (sampled rows + full heads)")
+    _sampled_check(w)
+
+
+def test_fwd_bf16_workload_causal_gqa_4096():
+    w = WORKLOADS["fwd_causal_gqa_bf16_b2hq64hkv8n4096d128"]
+    _say(f"workload {w.name} (sampled rows + full heads)")
+    _sampled_check(w, rows_per_head=16)
+
+
+def test_fwd_bf16_is_bitwise_repeatable():
+    import tiled_online_softmax_fa_amd as fa
+
+    inp_shape = (2, 8, 2, 1500, 128)
+    from fa_inputs import make_inputs
+
+    inp = make_inputs(*inp_shape, "bf16", seed=9)
+    q, k, v = (to_device(inp, n, "bf16") for n in ("q", "k", "v"))
+    torch = torch_mod()
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_empty_and_errors():
+    import tiled_online_softmax_fa_amd as fa
+
+    torch = torch_mod()
+    z = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    o, lse = fa.fwd(z, z, z, causal=True)
+    assert o.shape == (1, 2, 0, 64) and lse.shape == (1, 2, 0)
+    q = torch.zeros((1, 2, 8, 96), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    q = torch.zeros((1, 3, 8, 64), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, k, k)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
+    flat = torch.zeros(2 * 8 * 64 + 1, dtype=torch.bfloat16, device="cuda:0")
+    mis = flat[1:].view(1, 2, 8, 64)  # 2-byte offset: misaligned base pointer
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(mis, mis, mis)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG

@@ -1,0 +1,220 @@
+"""Exact tiled attention for AMD MI355X (gfx950): Python binding of libfa.
+
+Every step of the computation runs in libfa's HIP kernels; this module only
+checks tensor metadata, allocates outputs with torch (device memory), and
+passes raw pointers and the current stream through the C ABI declared in
+include/fa.h. There is no fallback: if libfa.so is missing or cannot be
+loaded, importing the ops raises.
+
+    o, lse = fwd(q, k, v, causal=True)              # bf16 [B,H,N,d]
+    o, lse = fwd_f32(q, k, v)                        # float32
+    dq, dk, dv = bwd(q, k, v, o, lse, dout, causal=True)
+    o = flash_attn(q, k, v, causal=True)             # autograd.Function
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH",
+    "FaError",
+    "load_library",
+    "fwd",
+    "fwd_f32",
+    "bwd",
+    "bwd_workspace_bytes",
+    "flash_attn",
+    "status_string",
+    "FA_OK",
+    "FA_ERR_INVALID_ARG",
+    "FA_ERR_UNSUPPORTED",
+    "FA_ERR_DEVICE",
+    "FA_ERR_LAUNCH",
+    "FA_ERR_INTERNAL",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_DEVICE = -3
+FA_ERR_LAUNCH = -4
+FA_ERR_INTERNAL = -5
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: libfa status {status} ({status_string(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once and declare the C signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libfa.so not found at {path}; build it with "
+                          "`python -m tiled_online_softmax_fa_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_f32.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != FA_OK:
+        raise FaError(status, what)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, Hq, k.shape[1], N, d
+
+
+def _require(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fwd_impl(entry, dtype, q, k, v, causal, scale, out, lse):
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, dtype, n)
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require(out, dtype, "out")
+    _require(lse, torch.float32, "lse")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    lib = load_library()
+    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                             int(bool(causal)), float(scale), _stream_ptr(q))
+    _check(st, entry)
+    return out, lse
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Forward attention on bf16 tensors (q [B,Hq,N,d], k/v [B,Hkv,N,d]). Returns (o, lse)."""
+    return _fwd_impl("fa_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Forward attention on float32 tensors. Returns (o, lse)."""
+    return _fwd_impl("fa_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse)
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward attention on bf16 tensors. Returns (dq, dk, dv)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, torch.bfloat16, n)
+    _require(lse, torch.float32, "lse")
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o/dout/lse have the wrong shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _require(t, torch.bfloat16, n)
+    need = bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    lib = load_library()
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                    _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                    _stream_ptr(q))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class FlashAttnFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            o, lse = fwd(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = bwd(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return FlashAttnFunction
+
+
+_FN = None
+
+
+def flash_attn(q, k, v, causal=False, scale=None):
+    """Differentiable exact attention on bf16 tensors (libfa forward and backward)."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _FN.apply(q, k, v, causal, scale)

@@ -1,0 +1,158 @@
+// C ABI of libfa: argument validation, device check, dispatch to the kernels.
+// Every check that depends only on the arguments runs before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shapes common to forward and backward. Returns FA_OK, or the error code.
+int check_shapes(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // every tensor must index with 32-bit element offsets inside one head and
+  // with size_t across heads; keep the whole tensor below 2^31 elements
+  const long long elems = (long long)B * Hq * N * d;
+  if (elems >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    if (p == nullptr) return FA_ERR_INVALID_ARG;
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+// gfx950 check for the current device, cached per device id.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return FA_OK;
+    if (st == 2) return FA_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T>
+int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+               int causal, float scale, hipStream_t stream, bool bf16) {
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q, k, v, o, lse});
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.scale_log2 = scale * kLog2e;
+  return launch_status(bf16 ? fa::launch_fwd_bf16(p, d, causal != 0, stream)
+                            : fa::launch_fwd_f32(p, d, causal != 0, stream));
+}
+
+size_t bwd_workspace(int B, int Hq, int N, int d) {
+  const size_t rows = (size_t)B * Hq * N;
+  const size_t delta = (rows * sizeof(float) + 255) & ~(size_t)255;
+  return delta + rows * (size_t)d * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, hipStream_t stream) {
+  return fwd_common<void>(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, true);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int N,
+               int d, int causal, float scale, hipStream_t stream) {
+  return fwd_common<float>(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, false);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f) != FA_OK) return 0;
+  return bwd_workspace(B, Hq, N, d);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, hipStream_t stream) {
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace});
+  if (st != FA_OK) return st;
+  if (workspace_bytes < bwd_workspace(B, Hq, N, d)) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const size_t rows = (size_t)B * Hq * N;
+  p.delta = (float*)workspace;
+  p.dq_acc = (float*)((char*)workspace + ((rows * sizeof(float) + 255) & ~(size_t)255));
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  return launch_status(fa::launch_bwd_bf16(p, d, causal != 0, stream));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, bad size, flag or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 64/128, or device is not gfx950)";
+    case FA_ERR_DEVICE: return "no usable HIP device";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

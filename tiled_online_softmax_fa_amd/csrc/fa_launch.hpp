@@ -1,0 +1,42 @@
+// Kernel parameter blocks and host-side launchers (C++ linkage, internal to libfa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N;
+  float scale_log2;  // scale * log2(e): scores are exponentiated with exp2
+  int n_tiles;       // query tiles per head (filled in by the launcher)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // [B, Hq, N] workspace: D_i = sum_c dout_ic o_ic
+  float* dq_acc;  // [B, Hq, N, d] workspace: fp32 dq accumulator
+  int B, Hq, Hkv, N;
+  float scale;
+  float scale_log2;
+  int n_tiles;
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa
