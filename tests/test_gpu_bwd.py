@@ -1,0 +1,136 @@
+"""Backward parity: libfa dQ, dK, dV on the GPU against the fp64 CPU oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from fa_inputs import WORKLOADS, make_inputs, make_workload_inputs
+from fa_testlib import assert_bf16_close, to_device, to_f64, torch_mod
+from oracle import attention_bwd, attention_bwd_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(inp, causal, scale):
+    import tiled_online_softmax_fa_amd as fa
+
+    q, k, v, dO = (to_device(inp, n, "bf16") for n in ("q", "k", "v", "dO"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dO, causal=causal, scale=scale)
+    torch_mod().cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check_grads(got, ref, what):
+    worst = []
+    for name, gt, rf in zip(("dQ", "dK", "dV"), got, ref):
+        s = float(np.abs(rf).max())
+        if s == 0.0:  # an exactly-zero gradient (e.g. a single key) must come out exactly zero
+            assert np.all(gt == 0), f"{what} {name}: expected exact zeros"
+            worst.append(f"{name} exact 0")
+            continue
+        mx, mean = assert_bf16_close(gt, rf, f"{what} {name}", scale=s)
+        worst.append(f"{name} max {mx / s:.1e} mean {mean / s:.1e}")
+    _say("  " + ", ".join(worst))
+
+
+SMALL = [
+    (1, 2, 2, 300, 64, False),
+    (1, 2, 2, 300, 64, True),
+    (1, 2, 2, 300, 128, False),
+    (1, 2, 2, 300, 128, True),
+    (2, 4, 2, 257, 128, True),
+    (1, 4, 1, 200, 64, True),
+    (1, 8, 1, 130, 128, False),
+    (1, 1, 1, 1, 128, True),
+    (1, 2, 2, 17, 64, False),
+    (1, 2, 2, 1000, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", SMALL)
+def test_bwd_small(B, Hq, Hkv, N, d, causal):
+    _say(f"bwd B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    inp = make_inputs(B, Hq, Hkv, N, d, "bf16", seed=N + 3 * d, backward=True)
+    scale = d ** -0.5
+    got = [to_f64(t) for t in _run(inp, causal, scale)]
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], causal, scale)
+    _check_grads(got, ref, "bwd")
+
+
+def test_bwd_peaky():
+    _say("bwd peaky q x 8")
+    inp = make_inputs(1, 4, 2, 500, 128, "bf16", seed=21, backward=True, q_mult=8.0)
+    got = [to_f64(t) for t in _run(inp, True, 128 ** -0.5)]
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], True, 128 ** -0.5)
+    _check_grads(got, ref, "bwd peaky")
+
+
+def test_bwd_workload_causal_4096():
+    w = WORKLOADS["bwd_causal_bf16_b2h16n4096d128"]
+    _say(f"workload {w.name}: full oracle on 3 heads, invariants on all heads")
+    inp = make_workload_inputs(w)
+    dq, dk, dv = (to_f64(t) for t in _run(inp, w.causal, w.scale))
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all()
+    for b, h in ((0, 0), (1, 7), (1, 15)):
+        ref = attention_bwd_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], inp["dO"][b, h], w.causal, w.scale)
+        _check_grads((dq[b, h], dk[b, h], dv[b, h]), ref, f"head ({b},{h})")
+    # any size: keys' gradients sum to zero (softmax is shift invariant) and
+    # sum_j dV_j = sum_i dO_i (probability rows sum to one)
+    dO = inp["dO"].astype(np.float64)
+    sdv = dv.sum(axis=2)
+    np.testing.assert_allclose(sdv, dO.sum(axis=2), atol=2e-2 * np.abs(sdv).max() + 0.25)
+    sdk = dk.sum(axis=2)
+    assert np.abs(sdk).max() <= 2e-2 * np.abs(dk).max() * 64
+
+
+def test_bwd_gqa_medium():
+    _say("bwd GQA B1 Hq8 Hkv2 N777 d128 causal")
+    inp = make_inputs(1, 8, 2, 777, 128, "bf16", seed=31, backward=True)
+    got = [to_f64(t) for t in _run(inp, True, 128 ** -0.5)]
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], True, 128 ** -0.5)
+    _check_grads(got, ref, "bwd gqa")
+
+
+def test_bwd_dk_dv_repeatable():
+    inp = make_inputs(1, 4, 4, 600, 128, "bf16", seed=41, backward=True)
+    a = _run(inp, True, 128 ** -0.5)
+    b = _run(inp, True, 128 ** -0.5)
+    torch = torch_mod()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    # dq uses fp32 atomics: order may differ, values within rounding
+    assert (a[0].float() - b[0].float()).abs().max().item() <= 1e-2
+
+
+def test_autograd_function():
+    import tiled_online_softmax_fa_amd as fa
+
+    torch = torch_mod()
+    inp = make_inputs(1, 2, 2, 150, 64, "bf16", seed=51, backward=True)
+    q, k, v, dO = (to_device(inp, n, "bf16").requires_grad_(n != "dO") for n in ("q", "k", "v", "dO"))
+    o = fa.flash_attn(q, k, v, causal=True)
+    o.backward(dO)
+    torch.cuda.synchronize()
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], True, 64 ** -0.5)
+    _check_grads([to_f64(t.grad) for t in (q, k, v)], ref, "autograd")
+
+
+def test_bwd_errors():
+    import tiled_online_softmax_fa_amd as fa
+
+    torch = torch_mod()
+    x = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda:0")
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ValueError):
+        fa.bwd(x, x, x, x, lse, x, workspace=small_ws)
+    z = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    zl = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = fa.bwd(z, z, z, z, zl, z)
+    assert dq.shape == z.shape
