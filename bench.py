@@ -1,0 +1,254 @@
+"""Throughput of the libfa attention path on one MI355X.
+
+One step = forward + backward of exact causal attention on the workload
+B=2, H=16, N=4096, d=128, bf16 storage, fp32 accumulation: fa_fwd (O, lse)
+followed by fa_bwd (dQ, dK, dV recomputed from lse), on seeded i.i.d. N(0,1)
+inputs already resident in device memory.
+
+Prints one JSON line. `value` is the step's algorithmic TFLOP/s:
+forward 4*B*H*N^2*d / 2 (causal) plus backward 2.5x that (five N^2*d matrix
+products instead of two), divided by the measured step time. Each kernel is
+also timed on its own with HIP events on the launch stream; `roofline`
+describes the kernel with the largest time per step.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+WORKLOAD = dict(B=2, H=16, N=4096, d=128, causal=True, seed=4)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """Raw HIP events through the runtime library (same stream the kernels use)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+
+def flops(B, H, N, d, causal):
+    fwd = 4.0 * B * H * N * N * d / (2.0 if causal else 1.0)
+    return fwd, 2.5 * fwd
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_online_softmax_fa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, launches_note):
+    """HBM bytes per launch from the committed PMC summary, if it is for the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inputs, budget_s=10.0):
+    """Time the fp64 oracle (fwd + bwd per head) on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_bwd_head, attention_fwd
+
+    w = WORKLOAD
+    scale = w["d"] ** -0.5
+    heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
+    t0 = time.perf_counter()
+    done = 0
+    for b, h in heads:
+        q, k, v, dO = (inputs[n][b:b + 1, h:h + 1] for n in ("q", "k", "v", "dO"))
+        attention_fwd(q, k, v, True, scale)
+        attention_bwd_head(q[0, 0], k[0, 0], v[0, 0], dO[0, 0], True, scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    f, b_ = flops(1, done, w["N"], w["d"], True)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": (f + b_) / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs of the same workload, fwd + bwd each, "
+                  f"fp64 NumPy with the full N x N matrix, {secs:.1f} s",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this library runs a single "
+              "MI355X; the multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tiled_online_softmax_fa_amd as fa
+    from fa_inputs import make_inputs
+
+    w = WORKLOAD
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    scale = d ** -0.5
+    log(f"generating inputs B{B} H{H} N{N} d{d} causal seed {w['seed']}")
+    inputs = make_inputs(B, H, H, N, d, "bf16", w["seed"], backward=True)
+    dev = {n: torch.from_numpy(inputs[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+           for n in ("q", "k", "v", "dO")}
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = (torch.empty_like(dev[n]) for n in ("q", "k", "v"))
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda:0")
+
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    K = args.steps
+    ev_f = [(hip.event(), hip.event()) for _ in range(K)]
+    ev_b = [(ctypes.c_void_p * 4)(*[hip.event() for _ in range(4)]) for _ in range(K)]
+    ev_all = (hip.event(), hip.event())
+
+    def step(i=None):
+        if i is not None:
+            hip.record(ev_f[i][0], stream)
+        fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale, out=o, lse=lse)
+        if i is not None:
+            hip.record(ev_f[i][1], stream)
+        fa.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["dO"], causal=causal, scale=scale, dq=dq, dk=dk, dv=dv,
+               workspace=ws, events=ev_b[i] if i is not None else None)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    hip.record(ev_all[0], stream)
+    for i in range(K):
+        step(i)
+    hip.record(ev_all[1], stream)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(*ev_all)
+    ms_step = total_ms / K
+    kern_ms = {
+        "fa_fwd_bf16_kernel": sum(hip.ms(a, b) for a, b in ev_f) / K,
+        "fa_bwd_pre_kernel": sum(hip.ms(e[0], e[1]) for e in ev_b) / K,
+        "fa_bwd_main_kernel": sum(hip.ms(e[1], e[2]) for e in ev_b) / K,
+        "fa_bwd_dq_convert_kernel": sum(hip.ms(e[2], e[3]) for e in ev_b) / K,
+    }
+    f_fwd, f_bwd = flops(B, H, N, d, causal)
+    elt = 2
+    qkv_bytes = B * H * N * d * elt
+    # algorithmic work per launch of each kernel
+    work = {
+        "fa_fwd_bf16_kernel": ("mfma", f_fwd),
+        "fa_bwd_main_kernel": ("mfma", f_bwd),
+        # reads o, dO; writes D (fp32) and zeroes the fp32 dQ accumulator
+        "fa_bwd_pre_kernel": ("hbm", 2 * qkv_bytes + 4 * B * H * N + 2 * qkv_bytes),
+        # reads the fp32 accumulator, writes bf16 dQ
+        "fa_bwd_dq_convert_kernel": ("hbm", 2 * qkv_bytes + qkv_bytes),
+    }
+    dominant = max(kern_ms, key=kern_ms.get)
+    bound, units = work[dominant]
+    avg_s = kern_ms[dominant] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = units / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = units / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": measured_traffic(dominant, "per launch"),
+                "avg_launch_us": kern_ms[dominant] * 1e3}
+    kernels = {}
+    for name, ms in kern_ms.items():
+        b_, u_ = work[name]
+        if b_ == "mfma":
+            kernels[name] = {"avg_us": ms * 1e3, "tflops": u_ / (ms * 1e-3) / 1e12,
+                             "frac_of_peak": u_ / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        else:
+            kernels[name] = {"avg_us": ms * 1e3, "gbs": u_ / (ms * 1e-3) / 1e9,
+                             "frac_of_peak": u_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    bwd_ms = kern_ms["fa_bwd_pre_kernel"] + kern_ms["fa_bwd_main_kernel"] + kern_ms["fa_bwd_dq_convert_kernel"]
+    result = {
+        "metric": "attention fwd+bwd TFLOPS (and % of MI355X bf16 dense MFMA peak), causal d=128 N=4096",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to bf16 (RNE)",
+        "config": {"workload": "causal attention fwd+bwd, B=2 H=16 N=4096 d=128, bf16 storage, fp32 accumulation",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "scale": scale},
+        "pct_of_peak": value / PEAK_BF16_TFLOPS * 100,
+        "fwd_tflops": f_fwd / (kern_ms["fa_fwd_bf16_kernel"] * 1e-3) / 1e12,
+        "fwd_pct_of_peak": f_fwd / (kern_ms["fa_fwd_bf16_kernel"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100,
+        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+        "bwd_pct_of_peak": f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100,
+        "kernels": kernels,
+        "roofline": roofline,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(inputs)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -89,6 +89,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            hipStream_t stream);
 
+/* Instrumentation variant of fa_bwd for measurement: identical arguments and
+ * results, plus `events`, an array of 4 hipEvent_t created by the caller (or
+ * NULL, then this is exactly fa_bwd). The events are recorded on `stream`
+ * before the row-term kernel, between it and the main kernel, between the
+ * main kernel and the dQ conversion, and after the conversion, so that each
+ * of the three kernels can be timed on its own. */
+int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                 hipStream_t stream, hipEvent_t* events);
+
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int status);
 

@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_f32.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp, vp]
+    lib.fa_bwd_timed.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -158,8 +160,12 @@ def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, N, d))
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
-    """Backward attention on bf16 tensors. Returns (dq, dk, dv)."""
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, events=None):
+    """Backward attention on bf16 tensors. Returns (dq, dk, dv).
+
+    events: optional ctypes array of 4 hipEvent_t handles; when given the call
+    goes through fa_bwd_timed, which records them around its three kernels.
+    """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _require(t, torch.bfloat16, n)
@@ -180,10 +186,12 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
     if workspace.numel() < need:
         raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
     lib = load_library()
-    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                    _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
-                    _stream_ptr(q))
-    _check(st, "fa_bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_ptr(q))
+    if events is None:
+        _check(lib.fa_bwd(*args), "fa_bwd")
+    else:
+        _check(lib.fa_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p)), "fa_bwd_timed")
     return dq, dk, dv
 
 

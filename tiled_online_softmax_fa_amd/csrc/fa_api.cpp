@@ -110,15 +110,19 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   return bwd_workspace(B, Hq, N, d);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-           void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
-           int causal, float scale, hipStream_t stream) {
+int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N,
+                 int d, int causal, float scale, hipStream_t stream, hipEvent_t* events) {
   int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
   if (B == 0 || N == 0) return FA_OK;
   st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace});
   if (st != FA_OK) return st;
   if (workspace_bytes < bwd_workspace(B, Hq, N, d)) return FA_ERR_INVALID_ARG;
+  if (events != nullptr) {
+    for (int i = 0; i < 4; ++i)
+      if (events[i] == nullptr) return FA_ERR_INVALID_ARG;
+  }
   st = check_device();
   if (st != FA_OK) return st;
   fa::BwdParams p{};
@@ -140,7 +144,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   p.N = N;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  return launch_status(fa::launch_bwd_bf16(p, d, causal != 0, stream));
+  return launch_status(fa::launch_bwd_bf16(p, d, causal != 0, stream, events));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, hipStream_t stream) {
+  return fa_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d, causal, scale,
+                      stream, nullptr);
 }
 
 const char* fa_status_string(int status) {

@@ -349,27 +349,31 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ launch
 template <int D, bool CAUSAL>
-static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream) {
+static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipEvent_t* ev) {
   BwdParams p = p_in;
   const long long rows = (long long)p.B * p.Hq * p.N;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
                      (const __bf16*)p.o, (const __bf16*)p.dout, p.delta, p.dq_acc, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + 127) / 128;
   hipLaunchKernelGGL((fa_bwd_main_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(256), 0, stream,
                      p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   const long long n4 = rows * D / 4;
   hipLaunchKernelGGL(fa_bwd_dq_convert_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p.dq_acc,
                      (__bf16*)p.dq, p.scale, n4);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_bwd_cfg<128, true>(p, stream) : launch_bwd_cfg<128, false>(p, stream);
-  if (d == 64) return causal ? launch_bwd_cfg<64, true>(p, stream) : launch_bwd_cfg<64, false>(p, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* ev) {
+  if (d == 128) return causal ? launch_bwd_cfg<128, true>(p, stream, ev) : launch_bwd_cfg<128, false>(p, stream, ev);
+  if (d == 64) return causal ? launch_bwd_cfg<64, true>(p, stream, ev) : launch_bwd_cfg<64, false>(p, stream, ev);
   return hipErrorInvalidValue;
 }
 

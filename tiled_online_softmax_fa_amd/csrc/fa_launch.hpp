@@ -37,6 +37,7 @@ struct BwdParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+// events: NULL or 4 events recorded before/between/after the three backward kernels
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* events);
 
 }  // namespace fa
