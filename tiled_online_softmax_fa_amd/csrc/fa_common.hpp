@@ -53,11 +53,39 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 // s_waitcnt encodings for gfx9: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // 16-byte direct global -> LDS copy: lane i writes lds_base + 16 * i.
 __device__ __forceinline__ void copy16_global_to_lds(const void* gsrc, lds_u8* lds_base) {
   __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)gsrc, (FA_LDS void*)lds_base, 16, 0, 0);
 }
+
+// The same 16-byte copy issued from inline assembly: `base` is a wave-uniform
+// global address, `voffset` this lane's byte offset from it, `lds_addr` the
+// wave-uniform LDS byte address written by lane 0 (lane i writes +16 i).
+// The compiler does not see the LDS write, so it inserts no wait for it:
+// the caller waits with wait_vmcnt0() before the barrier that publishes the
+// tile. M0 (the LDS address register of the instruction) is saved and
+// restored around the copy.
+__device__ __forceinline__ void copy16_global_to_lds_async(const void* base, uint32_t voffset, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voffset), "s"(lds_addr)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_u8* p) {
   return __builtin_bit_cast(bf16x8, *(const FA_LDS u32x4*)p);

@@ -10,12 +10,15 @@
 // Work decomposition (blogweb.cn sections 4-5: parallel over query blocks,
 // query block outer, key/value blocks inner; deepschool.ru "Flash Attention-2",
 // work partitioning: each warp owns its own rows):
-//   * one workgroup per (query tile of BM = NW * QPW rows, batch * head);
-//   * each of the NW waves owns QPW consecutive query rows and never exchanges
-//     partial results with another wave;
-//   * K/V tiles of BN keys are copied global -> LDS with 16-byte direct loads
-//     into a double buffer; the copy of tile j+1 is issued right after the
-//     single barrier of iteration j and overlaps the math of tile j.
+//   * one workgroup of 8 waves per (query tile of 256 rows, batch * head), two
+//     waves per SIMD; each wave owns 32 consecutive query rows and never
+//     exchanges partial results with another wave;
+//   * K/V tiles of 64 keys are copied global -> LDS with 16-byte direct loads
+//     into a ring of STAGES stages. The copy of tile t+STAGES-1 is issued
+//     right after the single barrier that publishes tile t+1, so it overlaps
+//     the math of STAGES-2 tiles ("Flash Attention V3技术解析" section 2.1,
+//     double buffering; one barrier per tile as in the aiknowledge.cn page,
+//     FA2 section 1).
 //
 // Orientation. Each wave computes S^T = K Q^T (keys on the accumulator's rows,
 // queries on its columns) with v_mfma_f32_16x16x32_bf16, so every lane owns
@@ -27,23 +30,31 @@
 // chunks against LDS bank conflicts (the padding idea of mhpq.cn section 5.2,
 // done by permuting chunks instead of padding rows).
 //
+// Software pipeline. A wave walks its keys in 32-key chunks. The steady-state
+// step for chunk c is one straight-line block holding the exponentials of c,
+// the S^T MFMAs of chunk c+1, the O^T += V^T P^T MFMAs of chunk c and the
+// row maximum of chunk c+1, so the matrix unit works on c+1 while the vector
+// unit finishes c (the softmax/GEMM overlap that "Flash Attention V3技术解析"
+// section 1.2 obtains with ping-pong warp groups, here inside one wave).
+// Chunks that need a mask (diagonal, end of sequence) take a plain path.
+//
 // Softmax bookkeeping, per query row, in the log2 domain (c = scale*log2 e):
 //   m  = reference maximum used for the exponentials,
 //   l  = per-lane partial sum of 2^(c s - m) (reduced over lanes at the end),
 //   acc = sum of 2^(c s - m) v (unnormalised).
-// A new tile only moves the reference maximum (and rescales l and acc by
+// A new chunk only moves the reference maximum (and rescales l and acc by
 // 2^(m_old - m_new), the correction of mhpq.cn section 2.2) when some score
 // exceeds m + kRescaleSlack. Otherwise the old reference is kept: every
 // exponential is then at most 2^kRescaleSlack, and because acc and l share
 // the same reference the ratio acc / l, i.e. O, is the same number. The check
-// is one compare per row and a wave vote, so the per-tile rescale of acc
-// (64-128 multiplies per lane) is skipped on almost every tile.
+// is one compare per row and a wave vote, so the per-chunk rescale of acc
+// (128 multiplies per lane) is skipped on almost every chunk.
 //
 // Causal (key j visible to query i iff j <= i): the key loop stops at the
 // last key tile holding a visible key for the workgroup's last query (tiles
 // wholly above the diagonal are never loaded, "Flash Attention V3技术解析"
-// section 2.1), each wave skips tiles above its own rows, and the element mask
-// is applied only on tiles that straddle the diagonal or the end of the
+// section 2.1), each wave stops at its own diagonal, and the element mask is
+// applied only on chunks that straddle the diagonal or the end of the
 // sequence.
 #include <type_traits>
 
@@ -65,29 +76,34 @@ struct KVSwizzle {
   __device__ static __forceinline__ int v_swz(int row) { return (row / kRowsPer256) % (kChunks16 / 2); }
 };
 
-template <int D, int QPW, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
-  constexpr int BM = QPW * NW;
+// Tuning knobs (instantiated by the launcher): QPW query rows per wave, NW
+// waves per workgroup, STAGES K/V tiles in the LDS ring. The register budget
+// follows from NW waves per CU: 8 waves put two on every SIMD, and the vector
+// phase of one overlaps the matrix phase of the other. PRIO raises the
+// wave's issue priority around its runs of matrix instructions, so the wave
+// that has MFMA work ready wins the issue slot and the other wave's vector
+// work fills the gaps.
+template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
+void fa_fwd_bf16_kernel(FwdParams p) {
+  constexpr int BM = QPW * NW, BN = 64;
+  constexpr int OPS = 2 * (BN * D * 2 / 1024) / NW;  // copy instructions per wave per tile (K and V)
+  static_assert(STAGES >= 3, "the copy of tile t+STAGES-1 is issued while tile t is read");
   constexpr int QB = QPW / 16;           // 16-query blocks per wave
   constexpr int DC = D / 32;             // k-steps of S^T = K Q^T
-  constexpr int KC = BN / 32;            // 32-key chunks per tile (= k-steps of O^T += V^T P^T)
   constexpr int DB = D / 16;             // 16-row blocks of O^T
+  constexpr int CPT = BN / 32;           // 32-key chunks per tile
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int COPIES = TILE_BYTES / 1024;       // 1 KiB (64 lanes x 16 B) per copy instruction
   constexpr int COPIES_PER_WAVE = COPIES / NW;
   constexpr int ROWS_PER_COPY = 1024 / (2 * D);
   constexpr int CH = 2 * D / 16;
   using Swz = KVSwizzle<D>;
-  static_assert(QPW % 16 == 0 && BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(COPIES % NW == 0, "K/V copy must split evenly over the waves");
 
-  // Two stages of (K, V). Four distinct arrays (not one indexed buffer) let
-  // the compiler see that the copy into one stage never aliases the reads of
-  // the other, so it does not wait for the in-flight copy before reading.
-  __shared__ __attribute__((aligned(1024))) unsigned char k_stage0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_stage0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_stage1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_stage1[TILE_BYTES];
+  // ring of STAGES x (K tile, V tile)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int N = p.N;
   const int lane = threadIdx.x & 63;
@@ -100,21 +116,23 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
   const int h = tc.head - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);
   const __bf16* __restrict__ qg = (const __bf16*)p.q + ((size_t)(b * p.Hq + h) * N) * D;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + ((size_t)(b * p.Hkv + hk) * N) * D;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + ((size_t)(b * p.Hkv + hk) * N) * D;
+  const __bf16* kg = (const __bf16*)p.k + ((size_t)(b * p.Hkv + hk) * N) * D;
+  const __bf16* vg = (const __bf16*)p.v + ((size_t)(b * p.Hkv + hk) * N) * D;
   __bf16* __restrict__ og = (__bf16*)p.o + ((size_t)(b * p.Hq + h) * N) * D;
   float* __restrict__ lseg = p.lse + (size_t)(b * p.Hq + h) * N;
 
   const int q0 = tc.tile * BM;
   const int qw0 = q0 + wave * QPW;  // first query row of this wave
-  const int qw_last = qw0 + QPW - 1;
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_kv = (kv_end + BN - 1) / BN;
-  const int n_kv_wave = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + BN - 1) / BN : 0;
+  const int n_kv = (kv_end + BN - 1) / BN;  // tiles loaded by the workgroup
+  // chunks this wave processes, and the first one that needs an element mask
+  const int n_ch = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
+  const int first_mask = min(n_ch, CAUSAL ? min((qw0 + 1) / 32, N / 32) : N / 32);
 
-  // Copy K/V tile `t`: this wave's COPIES_PER_WAVE pieces of 1 KiB each.
-  auto issue_tile_copy = [&](int t, lds_u8* kdst, lds_u8* vdst) __attribute__((always_inline)) {
+  // ---- K/V tile copies (asynchronous; published by the barrier of the tile)
+  auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t * BN;
+    const uint32_t kdst = lds_address(smem) + (t % STAGES) * 2 * TILE_BYTES;
 #pragma unroll
     for (int c = 0; c < COPIES_PER_WAVE; ++c) {
       const int piece = wave * COPIES_PER_WAVE + c;
@@ -123,12 +141,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
       const int grow = min(kv0 + prow, N - 1);              // rows past the end: any valid row, masked later
       const int kch = pch ^ Swz::k_swz(prow);
       const int vch = (((pch >> 1) ^ Swz::v_swz(prow)) << 1) | (pch & 1);
-      copy16_global_to_lds(kg + (size_t)grow * D + kch * 8, kdst + piece * 1024);
-      copy16_global_to_lds(vg + (size_t)grow * D + vch * 8, vdst + piece * 1024);
+      copy16_global_to_lds_async(kg, (uint32_t)(grow * D + kch * 8) * 2, kdst + piece * 1024);
+      copy16_global_to_lds_async(vg, (uint32_t)(grow * D + vch * 8) * 2, kdst + TILE_BYTES + piece * 1024);
     }
   };
 
-  if (n_kv > 0) issue_tile_copy(0, (lds_u8*)k_stage0, (lds_u8*)v_stage0);
+  for (int t = 0; t < STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
 
   // Q^T fragments (B operand of S^T = K Q^T), held for the whole key loop.
   bf16x8 qf[QB][DC];
@@ -153,56 +171,88 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
   }
   const float c = p.scale_log2;
 
-  // One 32-key chunk of tile t: S^T, mask, online softmax, O^T += V^T P^T.
-  auto chunk = [&](const lds_u8* kt, const lds_u8* vt, int kv0, int kc) __attribute__((always_inline)) {
-    const int key0 = kv0 + kc * 32;
-    if (CAUSAL && key0 > qw_last) return;  // chunk wholly above this wave's rows
+  // Lane parts of the LDS fragment addresses (the stage and chunk parts are
+  // compile-time constants at every use, so they fold into the instruction
+  // offsets and no address arithmetic runs per chunk).
+  int k_off[DC];  // K row L of a 16-key block, 16-byte chunk dc*4 + g (swizzled)
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) k_off[dc] = L * (2 * D) + (((dc * 4 + g) ^ Swz::k_swz(L)) * 16);
+  int v_off[DB];  // V row 4g + L/4 of a 32-key chunk, 32-byte chunk db (swizzled), 8 bytes at 8 (L & 3)
+  {
+    const int vrow = 4 * g + (L >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_off[db] = vrow * (2 * D) + ((db ^ Swz::v_swz(vrow)) * 32) + 8 * (L & 3);
+  }
+  static_assert(D == 64 || 16 % Swz::kRowsPer256 == 0, "swizzle period");
 
-    // ---- S^T for the two 16-key blocks of the chunk
-    f32x4 s[2][QB];
+  // K fragments (A operand of S^T) of chunk cc (0..CPT-1) of the tile in stage ST
+  auto read_k = [&](auto st, int cc, bf16x8 (&kf)[2][DC]) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    const lds_u8* kt = smem + ST * 2 * TILE_BYTES;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        kf[hb][dc] = lds_read_b128(kt + (cc * 32 + hb * 16) * (2 * D) + k_off[dc]);
+  };
+  // V^T fragments (A operand of O^T += V^T P^T): rows d = 16 db + lane % 16,
+  // element e < 4 -> key 4g + e, e >= 4 -> key 16 + 4g + e - 4 of the chunk
+  auto read_v = [&](auto st, int cc, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    const lds_u8* vt = smem + ST * 2 * TILE_BYTES + TILE_BYTES + cc * 32 * (2 * D);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo = lds_read_tr16_b64(vt + v_off[db]);
+      const i16x4 hi = lds_read_tr16_b64(vt + 16 * (2 * D) + v_off[db]);
+      vf[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto compute_s = [&](const bf16x8 (&kf)[2][DC], f32x4 (&s)[2][QB]) __attribute__((always_inline)) {
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int row = kc * 32 + hb * 16 + L;
-      bf16x8 kf[DC];
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const int ch = (dc * 4 + g) ^ Swz::k_swz(row);
-        kf[dc] = lds_read_b128(kt + row * (2 * D) + ch * 16);
-      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[hb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[hb][qb] = mfma_bf16_16x16x32(kf[dc], qf[qb][dc], s[hb][qb]);
+        for (int qb = 0; qb < QB; ++qb) s[hb][qb] = mfma_bf16_16x16x32(kf[hb][dc], qf[qb][dc], s[hb][qb]);
     }
-
-    // ---- mask: only chunks crossing the diagonal or the sequence end
-    if ((key0 + 32 > N) || (CAUSAL && key0 + 31 > qw0)) {
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  auto apply_mask = [&](int ch, f32x4 (&s)[2][QB]) __attribute__((always_inline)) {
+    const int key0 = ch * 32;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = key0 + hb * 16 + g * 4 + r;
-            const int qi = qw0 + qb * 16 + L;
-            const bool visible = key < N && (!CAUSAL || key <= qi);
-            s[hb][qb][r] = visible ? s[hb][qb][r] : kNegInf;
-          }
-    }
-
-    // ---- online softmax: move the reference maximum only when needed
-    float tmax[QB];
-    bool grow = false;
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + hb * 16 + g * 4 + r;
+          const int qi = qw0 + qb * 16 + L;
+          const bool visible = key < N && (!CAUSAL || key <= qi);
+          s[hb][qb][r] = visible ? s[hb][qb][r] : kNegInf;
+        }
+  };
+  // in-lane maximum of the chunk per query block, scaled to log2 units
+  auto chunk_max = [&](const f32x4 (&s)[2][QB], float (&tmax)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3]));
-      mx = fmaxf(mx, fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
-      tmax[qb] = mx * c;
-      grow |= tmax[qb] > m_ref[qb] + kRescaleSlack;
+      float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
+      mx = fmaxf(fmaxf(mx, s[0][qb][3]), s[1][qb][0]);
+      mx = fmaxf(fmaxf(mx, s[1][qb][1]), s[1][qb][2]);
+      tmax[qb] = fmaxf(mx, s[1][qb][3]) * c;
     }
+  };
+  // move the reference maximum if some score exceeds it by more than the slack
+  auto update_reference = [&](const float (&tmax)[QB]) __attribute__((always_inline)) {
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) grow |= tmax[qb] > m_ref[qb] + kRescaleSlack;
     if (wave_any(grow)) {
+      // rare path: the marker keeps the compiler from turning this branch
+      // into unconditional selects executed on every chunk
+      asm volatile("; reference maximum moves" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float m_new = fmaxf(m_ref[qb], max_over_row_groups(tmax[qb]));
@@ -213,10 +263,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
       }
     }
-
-    // ---- P^T = 2^(c S^T - m) packed to bf16 in the B-operand layout of O^T += V^T P^T:
-    // element e < 4 -> key key0 + 4g + e, element e >= 4 -> key key0 + 16 + 4g + e - 4.
-    bf16x8 pf[QB];
+  };
+  // P^T = 2^(c S^T - m), packed to bf16 in the B-operand layout of O^T += V^T P^T
+  auto exponentiate = [&](const f32x4 (&s)[2][QB], bf16x8 (&pf)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float neg_m = -m_ref[qb];
@@ -226,44 +275,104 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
         e[r] = exp2_fast(fmaf(s[0][qb][r], c, neg_m));
         e[4 + r] = exp2_fast(fmaf(s[1][qb][r], c, neg_m));
       }
-      l_part[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       u32x4 packed = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                       pack_bf16x2(e[6], e[7])};
+      l_part[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       pf[qb] = __builtin_bit_cast(bf16x8, packed);
     }
+  };
+  auto accumulate_pv = [&](const bf16x8 (&vf)[DB], const bf16x8 (&pf)[QB]) __attribute__((always_inline)) {
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma_bf16_16x16x32(vf[db], pf[qb], acc[db][qb]);
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
 
-    // ---- O^T += V^T P^T; A operand rows d = 16db + (lane % 16), keys ordered as in pf
-    const int vrow0 = kc * 32 + 4 * g + (L >> 2);
-    const int vrow1 = vrow0 + 16;
-    const int within = 8 * (L & 3);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x4 lo = lds_read_tr16_b64(vt + vrow0 * (2 * D) + ((db ^ Swz::v_swz(vrow0)) * 32) + within);
-      const i16x4 hi = lds_read_tr16_b64(vt + vrow1 * (2 * D) + ((db ^ Swz::v_swz(vrow1)) * 32) + within);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma_bf16_16x16x32(vf, pf[qb], acc[db][qb]);
+  // S^T of the chunk about to be exponentiated (masked, maximum folded in)
+  f32x4 s_cur[2][QB];
+
+  // S^T of chunk ch (in stage ST, position cc), masked when MASK, and the reference update.
+  auto scores = [&](auto st, int cc, int ch, auto mask) __attribute__((always_inline)) {
+    bf16x8 kf[2][DC];
+    read_k(st, cc, kf);
+    compute_s(kf, s_cur);
+    if (decltype(mask)::value) apply_mask(ch, s_cur);
+    float tmax[QB];
+    chunk_max(s_cur, tmax);
+    update_reference(tmax);
+  };
+
+  // Chunk ch (S^T in s_cur, reference current): exponentials and O^T += V^T P^T
+  // of ch, then S^T and the maximum of chunk ch+1. In the steady state (chunk
+  // ch+1 needs no mask) all of it up to the vote on ch+1 is one straight-line
+  // block, so the scheduler overlaps the exponentials of ch with the matrix
+  // work of ch+1. ST/CC: stage and position of ch; STN/CCN: those of ch+1.
+  auto chunk_step = [&](auto st, auto cc, auto stn, auto ccn, int ch) __attribute__((always_inline)) {
+    bf16x8 vf[DB], pf[QB];
+    if (ch + 1 < first_mask) {
+      read_v(st, cc, vf);
+      exponentiate(s_cur, pf);
+      accumulate_pv(vf, pf);
+      scores(stn, ccn, ch + 1, std::false_type{});
+    } else {
+      read_v(st, cc, vf);
+      exponentiate(s_cur, pf);
+      accumulate_pv(vf, pf);
+      if (ch + 1 < n_ch) scores(stn, ccn, ch + 1, std::true_type{});
     }
   };
 
-  // One key tile: one barrier, prefetch of the next tile into the other stage, math.
-  auto tile = [&](auto stage, int t) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage)::value;
-    lds_u8* kcur = (lds_u8*)(S == 0 ? k_stage0 : k_stage1);
-    lds_u8* vcur = (lds_u8*)(S == 0 ? v_stage0 : v_stage1);
-    lds_u8* knext = (lds_u8*)(S == 0 ? k_stage1 : k_stage0);
-    lds_u8* vnext = (lds_u8*)(S == 0 ? v_stage1 : v_stage0);
-    wait_vmcnt0();     // this wave's copies of tile t have landed
-    __syncthreads();   // ... and every other wave's; all reads of tile t-1 are done
-    if (t + 1 < n_kv) issue_tile_copy(t + 1, knext, vnext);
-    if (t >= n_kv_wave) return;  // tile lies wholly above this wave's rows
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) chunk(kcur, vcur, t * BN, kc);
+  // ---- key loop: tiles in workgroup lock-step, chunks per wave. The last
+  // chunk of tile t reads K of tile t+1, so tile t+1 is published by the
+  // barrier just before it; at that point every wave is done with tile t-1,
+  // whose stage receives tile t+STAGES-1. The loop is unrolled over the
+  // STAGES stages so that every LDS address has a constant stage part.
+  if (n_kv > 0) {
+    if (n_kv >= STAGES - 1) {
+      wait_vmcnt_le<(STAGES - 2) * OPS>();  // tile 0 landed; tiles 1..STAGES-2 may still fly
+    } else {
+      wait_vmcnt0();
+    }
+    __syncthreads();
+    if (n_ch > 0) {
+      if (first_mask > 0) {
+        scores(std::integral_constant<int, 0>{}, 0, 0, std::false_type{});
+      } else {
+        scores(std::integral_constant<int, 0>{}, 0, 0, std::true_type{});
+      }
+    }
+  }
+  auto tile = [&](auto st, int t) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int STN = (ST + 1) % STAGES;
+    static_assert(CPT == 2, "two 32-key chunks per tile");
+    // chunk 0 of tile t: next chunk in the same tile
+    if (2 * t < n_ch)
+      chunk_step(st, std::integral_constant<int, 0>{}, st, std::integral_constant<int, 1>{}, 2 * t);
+    // chunk 1 of tile t reads K of tile t+1: publish it first
+    if (t + 1 < n_kv) {
+      if (t + STAGES - 2 < n_kv) {
+        wait_vmcnt_le<(STAGES - 3) * OPS>();  // tile t+1 landed; tiles up to t+STAGES-2 may fly
+      } else {
+        wait_vmcnt0();
+      }
+      __syncthreads();
+      if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
+    }
+    if (2 * t + 1 < n_ch)
+      chunk_step(st, std::integral_constant<int, 1>{}, std::integral_constant<int, STN>{},
+                 std::integral_constant<int, 0>{}, 2 * t + 1);
   };
-
-  for (int t = 0; t < n_kv; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_kv) tile(std::integral_constant<int, 1>{}, t + 1);
+  for (int t0 = 0; t0 < n_kv; t0 += STAGES) {
+    tile(std::integral_constant<int, 0>{}, t0);
+    if (t0 + 1 < n_kv) tile(std::integral_constant<int, 1>{}, t0 + 1);
+    if (t0 + 2 < n_kv) tile(std::integral_constant<int, 2>{}, t0 + 2);
+    if constexpr (STAGES > 3) {
+      if (t0 + 3 < n_kv) tile(std::integral_constant<int, 3 % STAGES>{}, t0 + 3);
+    }
+    static_assert(STAGES <= 4, "unrolled for up to 4 stages");
   }
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
@@ -285,25 +394,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int D, int QPW, int NW, int BN, bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream) {
-  constexpr int BM = QPW * NW;
+  constexpr int QPW = 32, NW = 8, STAGES = 4;
   FwdParams p = p_in;
-  p.n_tiles = (p.N + BM - 1) / BM;
+  p.n_tiles = (p.N + QPW * NW - 1) / (QPW * NW);
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, QPW, NW, BN, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, QPW, NW, true, STAGES>), dim3(grid), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) {
-    return causal ? launch_fwd_bf16_cfg<128, 64, 4, 64, true>(p, stream)
-                  : launch_fwd_bf16_cfg<128, 64, 4, 64, false>(p, stream);
-  }
-  if (d == 64) {
-    return causal ? launch_fwd_bf16_cfg<64, 64, 4, 64, true>(p, stream)
-                  : launch_fwd_bf16_cfg<64, 64, 4, 64, false>(p, stream);
-  }
+  if (d == 128) return causal ? launch_fwd_bf16_cfg<128, true>(p, stream) : launch_fwd_bf16_cfg<128, false>(p, stream);
+  if (d == 64) return causal ? launch_fwd_bf16_cfg<64, true>(p, stream) : launch_fwd_bf16_cfg<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 
