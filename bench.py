@@ -89,6 +89,72 @@ def measured_traffic(kernel_key, launches_note):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 1 << 29  # 512 MiB read and 512 MiB written per calibration copy
+COPY_LAUNCHES = 4
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of known size, profiled to scale the byte counters."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(COPY_LAUNCHES):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": COPY_LAUNCHES}), flush=True)
+    return 0
+
+
+def _counter_per_dispatch(path, counter):
+    """Mean value of one counter per dispatch, per kernel name, from a rocprofv3 counter_collection CSV."""
+    import csv
+    from collections import defaultdict
+
+    tot, disp = defaultdict(float), defaultdict(set)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            tot[name] += float(r["Counter_Value"])
+            disp[name].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """profiles/traffic.json: HBM bytes per launch of each kernel (FETCH_SIZE + WRITE_SIZE, KiB per dispatch),
+    each counter scaled so that it reads the known size on a plain copy kernel."""
+    def copy_reading(path, counter):
+        per = _counter_per_dispatch(path, counter)
+        name = max(per, key=per.get)  # the copy is by far the largest dispatch of the calibration run
+        return name, per[name] * 1024.0
+
+    cname, cf = copy_reading(copy_fetch_csv, "FETCH_SIZE")
+    _, cw = copy_reading(copy_write_csv, "WRITE_SIZE")
+    f_fetch, f_write = COPY_BYTES / cf, COPY_BYTES / cw
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for key in ("fa_fwd_bf16_kernel", "fa_bwd_pre_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"):
+        fk = [n for n in fetch if key in n]
+        wk = [n for n in write if key in n]
+        if not fk or not wk:
+            continue
+        rd = fetch[fk[0]] * 1024.0 * f_fetch
+        wr = write[wk[0]] * 1024.0 * f_write
+        kernels[key] = {"hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr}
+    out = {
+        "source_digest": source_digest(),
+        "workload": "causal attention fwd+bwd, B=2 H=16 N=4096 d=128 (bench.py default)",
+        "calibration": {"kernel": cname, "copy_bytes": COPY_BYTES, "fetch_factor": f_fetch, "write_factor": f_write},
+        "kernels": kernels,
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def cpu_baseline(inputs, budget_s=10.0):
     """Time the fp64 oracle (fwd + bwd per head) on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_info
@@ -127,7 +193,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-warmup-s", type=float, default=WARMUP_MIN_S,
+                    help="keep warming up until this many seconds have passed (0 for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling the HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs "
+                         "of a short bench run and of a --copy-calibration run (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this library runs a single "
               "MI355X; the multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
@@ -135,6 +210,9 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     import tiled_online_softmax_fa_amd as fa
     from fa_inputs import make_inputs
@@ -169,10 +247,10 @@ def main():
 
     # W steps, then more until the warm-up has run for WARMUP_MIN_S: the
     # GPU clocks ramp up over the first second or so of sustained work
-    log(f"warmup {args.warmup} steps (at least {WARMUP_MIN_S} s)")
+    log(f"warmup {args.warmup} steps (at least {args.min_warmup_s} s)")
     t_w = time.perf_counter()
     n_w = 0
-    while n_w < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while n_w < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         step()
         n_w += 1
         if n_w % 4 == 0:
@@ -190,21 +268,24 @@ def main():
     kern_ms = {
         "fa_fwd_bf16_kernel": sum(hip.ms(a, b) for a, b in ev_f) / K,
         "fa_bwd_pre_kernel": sum(hip.ms(e[0], e[1]) for e in ev_b) / K,
-        "fa_bwd_main_kernel": sum(hip.ms(e[1], e[2]) for e in ev_b) / K,
-        "fa_bwd_dq_convert_kernel": sum(hip.ms(e[2], e[3]) for e in ev_b) / K,
+        "fa_bwd_dkdv_kernel": sum(hip.ms(e[1], e[2]) for e in ev_b) / K,
+        "fa_bwd_dq_kernel": sum(hip.ms(e[2], e[3]) for e in ev_b) / K,
     }
     f_fwd, f_bwd = flops(B, H, N, d, causal)
     elt = 2
     qkv_bytes = B * H * N * d * elt
     # algorithmic work per launch of each kernel
+    # The backward's algorithmic work is 5 products (S, dP, dV, dK, dQ: 2.5x the
+    # forward). The dK/dV kernel does 4 of them; the dQ kernel does the 5th and
+    # recomputes S and dP for it (executed, not counted as algorithmic work).
     work = {
         "fa_fwd_bf16_kernel": ("mfma", f_fwd),
-        "fa_bwd_main_kernel": ("mfma", f_bwd),
-        # reads o, dO; writes D (fp32) and zeroes the fp32 dQ accumulator
-        "fa_bwd_pre_kernel": ("hbm", 2 * qkv_bytes + 4 * B * H * N + 2 * qkv_bytes),
-        # reads the fp32 accumulator, writes bf16 dQ
-        "fa_bwd_dq_convert_kernel": ("hbm", 2 * qkv_bytes + qkv_bytes),
+        # reads o, dO; writes D (fp32)
+        "fa_bwd_pre_kernel": ("hbm", 2 * qkv_bytes + 4 * B * H * N),
+        "fa_bwd_dkdv_kernel": ("mfma", f_bwd * 4 / 5),
+        "fa_bwd_dq_kernel": ("mfma", f_bwd * 1 / 5),
     }
+    executed = {"fa_bwd_dq_kernel": f_bwd * 3 / 5}
     dominant = max(kern_ms, key=kern_ms.get)
     bound, units = work[dominant]
     avg_s = kern_ms[dominant] * 1e-3
@@ -221,11 +302,13 @@ def main():
         if b_ == "mfma":
             kernels[name] = {"avg_us": ms * 1e3, "tflops": u_ / (ms * 1e-3) / 1e12,
                              "frac_of_peak": u_ / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            if name in executed:
+                kernels[name]["executed_tflops"] = executed[name] / (ms * 1e-3) / 1e12
         else:
             kernels[name] = {"avg_us": ms * 1e3, "gbs": u_ / (ms * 1e-3) / 1e9,
                              "frac_of_peak": u_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    bwd_ms = kern_ms["fa_bwd_pre_kernel"] + kern_ms["fa_bwd_main_kernel"] + kern_ms["fa_bwd_dq_convert_kernel"]
+    bwd_ms = kern_ms["fa_bwd_pre_kernel"] + kern_ms["fa_bwd_dkdv_kernel"] + kern_ms["fa_bwd_dq_kernel"]
     result = {
         "metric": "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak, d=128 N=4096",
         "value": value,

@@ -81,8 +81,8 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  * heads dk and dv sum over the query heads that read each key/value head.
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, contents ignored on entry (float32 scratch for the row
- * term D_i = sum_c dout_ic o_ic and the float32 dq accumulator).
- * Supported d: 64, 128. */
+ * term D_i = sum_c dout_ic o_ic). All three outputs are bitwise repeatable
+ * (no atomics). Supported d: 64, 128. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,
@@ -92,9 +92,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 /* Instrumentation variant of fa_bwd for measurement: identical arguments and
  * results, plus `events`, an array of 4 hipEvent_t created by the caller (or
  * NULL, then this is exactly fa_bwd). The events are recorded on `stream`
- * before the row-term kernel, between it and the main kernel, between the
- * main kernel and the dQ conversion, and after the conversion, so that each
- * of the three kernels can be timed on its own. */
+ * before the row-term kernel, between it and the dK/dV kernel, between the
+ * dK/dV kernel and the dQ kernel, and after the dQ kernel, so that each of
+ * the three kernels can be timed on its own. */
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,

@@ -87,8 +87,8 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
 
 size_t bwd_workspace(int B, int Hq, int N, int d) {
   const size_t rows = (size_t)B * Hq * N;
-  const size_t delta = (rows * sizeof(float) + 255) & ~(size_t)255;
-  return delta + rows * (size_t)d * sizeof(float);
+  (void)d;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;  // D_i per query row
 }
 
 }  // namespace
@@ -137,7 +137,6 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   p.dv = dv;
   const size_t rows = (size_t)B * Hq * N;
   p.delta = (float*)workspace;
-  p.dq_acc = (float*)((char*)workspace + ((rows * sizeof(float) + 255) & ~(size_t)255));
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

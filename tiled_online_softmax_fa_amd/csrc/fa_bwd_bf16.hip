@@ -11,30 +11,36 @@
 // Grouped heads: the dK and dV of a key/value head sum over its query heads.
 //
 // Three kernels on the caller's stream:
-//   1. row term D (fp32) and zeroing of the fp32 dQ accumulator;
-//   2. one workgroup per (key tile of 128 keys, batch * key/value head): K, V
-//      of the tile stay in registers, each of the 4 waves owns 32 keys and
-//      accumulates their dK^T, dV^T; query tiles of 64 rows (Q, dO) stream
-//      through LDS (the tiled backward of the page "Flash Attention-2"
+//   1. row term D (fp32);
+//   2. dK, dV: one workgroup per (key tile of 128 keys, batch * key/value
+//      head): K, V of the tile stay in registers, each of the 4 waves owns 32
+//      keys and accumulates their dK^T, dV^T; query tiles of 64 rows (Q, dO)
+//      stream through LDS (the tiled backward of the page "Flash Attention-2"
 //      (deepschool.ru), "Улучшение backward pass", and blogweb.cn section 5).
 //      S = Q K^T is computed with keys on the accumulator's columns, so P and
 //      dS come out of the MFMA in the B-operand layout of dV^T += dO^T P and
 //      dK^T += Q^T dS, whose dO^T / Q^T fragments are transposing LDS reads.
-//      dQ needs the contraction over keys, so dS goes through LDS once and
-//      dQ += dS K is added to the fp32 accumulator with atomic adds (the dQ
-//      atomics of "Flash Attention V3技术解析" section 2.1);
-//   3. dQ = bf16(scale * accumulator).
+//      For grouped heads the query loop covers every query head of the
+//      group, so dK and dV are summed in registers;
+//   3. dQ: one workgroup per (query tile, batch * query head), built like
+//      the forward kernel: Q and dO stay in registers and K, V tiles stream
+//      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
+//      accumulates dQ^T += K^T dS^T. Recomputing S and dP here costs two
+//      more matrix products per tile than accumulating dQ inside kernel 2,
+//      but kernel 2 would have to add every key tile's contribution to dQ in
+//      memory (the atomics of "Flash Attention V3技术解析" section 2.1); the
+//      separate pass needs no atomics, no fp32 accumulator, and gives a
+//      bitwise repeatable dQ.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 
-// ------------------------------------------------------------------ kernel 1: D and zeroed dQ accumulator
+// ------------------------------------------------------------------ kernel 1: D
 // 16 lanes per row, 16 rows per workgroup of 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                         float* __restrict__ delta, float* __restrict__ dq_acc,
-                                                         long long rows) {
+                                                         float* __restrict__ delta, long long rows) {
   constexpr int PER_LANE = D / 16;  // 8 (d=128) or 4 (d=64) elements
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -44,9 +50,6 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const __bf16* __restric
     const __bf16* pd = dout + row * D + sub * PER_LANE;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) s = fmaf((float)po[i], (float)pd[i], s);
-    float* z = dq_acc + row * D + sub * PER_LANE;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; i += 4) *(f32x4*)(z + i) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   s += __shfl_xor(s, 8, 16);
   s += __shfl_xor(s, 4, 16);
@@ -55,17 +58,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const __bf16* __restric
   if (row < rows && sub == 0) delta[row] = s;
 }
 
-// ------------------------------------------------------------------ kernel 3: dQ = bf16(scale * acc)
-__global__ __launch_bounds__(256) void fa_bwd_dq_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
-                                                                float scale, long long n4) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const f32x4 a = ((const f32x4*)acc)[i] * scale;
-  u32x2 packed = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-  ((u32x2*)dq)[i] = packed;
-}
-
-// ------------------------------------------------------------------ kernel 2: main
+// ------------------------------------------------------------------ kernel 2: dK, dV
 template <int D>
 struct TileSwizzle {  // 16-byte chunk XOR swizzle of a row-major [rows][D] bf16 tile
   static constexpr int kRowBytes = 2 * D;
@@ -80,16 +73,15 @@ struct TileSwizzle {  // 16-byte chunk XOR swizzle of a row-major [rows][D] bf16
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = 4, KPW = 32, BNK = NW * KPW;  // 128 keys per workgroup
   constexpr int BMQ = 64;                          // query rows per step
-  constexpr int QB = BMQ / 16, KB = KPW / 16, QC = BMQ / 32, KC = BNK / 32;
+  constexpr int QB = BMQ / 16, KB = KPW / 16, QC = BMQ / 32;
   constexpr int DC = D / 32, DB = D / 16;
   constexpr int QTILE_BYTES = BMQ * D * 2;
   constexpr int COPIES_PER_WAVE = QTILE_BYTES / 1024 / NW;
   constexpr int ROWS_PER_COPY = 1024 / (2 * D);
   constexpr int CH = 2 * D / 16;
-  constexpr int DST_ROW_BYTES = BMQ * 2;  // dS^T tile row: 64 queries
   using Swz = TileSwizzle<D>;
   static_assert(COPIES_PER_WAVE >= 1, "tile copy split");
 
@@ -97,8 +89,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char do_stage0[QTILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char q_stage1[QTILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char do_stage1[QTILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_tile[BNK * D * 2];
-  __shared__ __attribute__((aligned(1024))) unsigned char dst_tile[BNK * DST_ROW_BYTES];
 
   const int N = p.N;
   const int lane = threadIdx.x & 63;
@@ -115,13 +105,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
   const __bf16* __restrict__ kg = (const __bf16*)p.k + kv_head * D;
   const __bf16* __restrict__ vg = (const __bf16*)p.v + kv_head * D;
 
-  // K tile (all 128 keys) into LDS for dQ += dS K; K^T, V^T fragments of this
-  // wave's keys into registers (B operands of S = Q K^T and dP = dO V^T).
-  for (int i = threadIdx.x; i < BNK * D / 8; i += NW * 64) {
-    const int row = i / (D / 8), c8 = i % (D / 8);
-    const int grow = min(kv0 + row, N - 1);
-    *(FA_LDS u32x4*)((lds_u8*)k_tile + Swz::offset(row, c8 * 8)) = *(const u32x4*)(kg + (size_t)grow * D + c8 * 8);
-  }
+  // K^T, V^T fragments of this wave's keys into registers (B operands of
+  // S = Q K^T and dP = dO V^T).
   bf16x8 kf[KB][DC], vf[KB][DC];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -177,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
     lds_u8* qt = (lds_u8*)(ST == 0 ? q_stage0 : q_stage1);
     lds_u8* dt = (lds_u8*)(ST == 0 ? do_stage0 : do_stage1);
     wait_vmcnt0();
-    __syncthreads();  // tile s landed; dS^T of step s-1 fully consumed
+    __syncthreads();  // tile s landed; every wave is done with tile s-1
     if (s + 1 < n_steps) issue_copy(s + 1, (lds_u8*)(ST == 0 ? q_stage1 : q_stage0),
                                     (lds_u8*)(ST == 0 ? do_stage1 : do_stage0));
     int h, i;
@@ -243,9 +228,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
           }
           pp[half][kb] = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
           dd[half][kb] = u32x2{pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3])};
-          // dS^T tile for dQ: row = key within the workgroup tile, 4 consecutive queries
-          *(FA_LDS u32x2*)((lds_u8*)dst_tile + (wave * KPW + kb * 16 + L) * DST_ROW_BYTES + (qb * 16 + 4 * g) * 2) =
-              dd[half][kb];
         }
       }
       // B-operand packing: elements 0..3 <- query block 2qc (rows 4g + e), 4..7 <- block 2qc + 1
@@ -277,48 +259,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
       }
     }
 
-    __syncthreads();  // dS^T complete
-
-    // ---- dQ[q, d] += sum over the tile's keys of dS[q, key] K[key, d]; wave w owns d-blocks {2w, 2w+1} (d=128)
-    constexpr int DBW = DB / NW;  // d-blocks per wave
-    f32x4 dq[QB][DBW];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int j = 0; j < DBW; ++j) dq[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int r0 = kc * 32 + 4 * g + (L >> 2), r1 = r0 + 16;
-      bf16x8 kB[DBW];
-#pragma unroll
-      for (int j = 0; j < DBW; ++j) {
-        const int col = (wave * DBW + j) * 16 + 4 * (L & 3);
-        const i16x4 lo = lds_read_tr16_b64((lds_u8*)k_tile + Swz::offset(r0, col));
-        const i16x4 hi = lds_read_tr16_b64((lds_u8*)k_tile + Swz::offset(r1, col));
-        kB[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int col = qb * 16 + 4 * (L & 3);
-        const i16x4 lo = lds_read_tr16_b64((lds_u8*)dst_tile + r0 * DST_ROW_BYTES + col * 2);
-        const i16x4 hi = lds_read_tr16_b64((lds_u8*)dst_tile + r1 * DST_ROW_BYTES + col * 2);
-        const bf16x8 sA = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int j = 0; j < DBW; ++j) dq[qb][j] = mfma_bf16_16x16x32(sA, kB[j], dq[qb][j]);
-      }
-    }
-    float* dqa = p.dq_acc + qh * D;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = q0 + qb * 16 + 4 * g + r;
-        if (qi < N) {
-#pragma unroll
-          for (int j = 0; j < DBW; ++j)
-            unsafeAtomicAdd(dqa + (size_t)qi * D + (wave * DBW + j) * 16 + L, dq[qb][j][r]);
-        }
-      }
   };
 
   if (n_steps > 0) issue_copy(0, (lds_u8*)q_stage0, (lds_u8*)do_stage0);
@@ -347,6 +287,247 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_main_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ kernel 3: dQ
+//
+// Tiles here are read both row-wise (16-byte reads of one row's chunk) and
+// transposed (ds_read_b64_tr_b16), so the 16-byte chunk c of row r is stored
+// at chunk c ^ f(r), with f chosen so that both access patterns spread over
+// the banks: f maps the 8 (16) consecutive rows of a row-wise read to
+// distinct chunks, and the rows 4g..4g+3 of a transposed read (two adjacent
+// chunks each) to 8 distinct chunks.
+template <int D>
+struct DualSwizzle {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = kRowBytes / 16;
+  __device__ static __forceinline__ int f(int row) {
+    int x = ((row & 3) << 1) | ((row >> 2) & 1);
+    if (kChunks == 16) x |= ((row >> 3) & 1) << 3;
+    return x;
+  }
+};
+
+// One workgroup of 8 waves per (query tile of 256 rows, batch * query head);
+// each wave owns 32 query rows. Per 32-key chunk, with keys on the
+// accumulator rows and queries on its columns (as in the forward kernel):
+//   S^T = K Q^T, dP^T = V dO^T                         (A: K, V rows from LDS)
+//   P^T = 2^(c S^T - lse log2 e), dS^T = P^T o (dP^T - D)   (per lane: one query)
+//   dQ^T += K^T dS^T          (A: transposing reads of the K tile, B: dS^T packed)
+// dQ = scale * dQ^T at the end. K/V tiles of 64 keys stream through a ring of
+// STAGES stages with asynchronous direct copies, one barrier per tile.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
+void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int QPW = 32, NW = 8, BM = QPW * NW, BN = 64, STAGES = 3;
+  constexpr int QB = QPW / 16, DC = D / 32, DB = D / 16;
+  constexpr int RB = 2 * D;  // bytes per tile row
+  constexpr int DO_BYTES = QB * DC * 64 * 16;  // one wave's dO^T fragments
+  constexpr int TILE_BYTES = BN * RB;
+  constexpr int COPIES_PER_WAVE = TILE_BYTES / 1024 / NW;
+  constexpr int OPS = 2 * COPIES_PER_WAVE;  // copy instructions per wave per tile (K and V)
+  constexpr int ROWS_PER_COPY = 1024 / RB;
+  constexpr int CH = RB / 16;
+  using Swz = DualSwizzle<D>;
+  static_assert(COPIES_PER_WAVE >= 1 && TILE_BYTES % (1024 * NW) == 0, "K/V copy must split evenly over the waves");
+
+  // K/V ring, then each wave's dO^T fragments (kept in LDS rather than in
+  // registers: with two waves per SIMD the register file holds Q^T, the dQ^T
+  // accumulator and one chunk's working set, but not dO^T as well)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES + NW * DO_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_raw;
+
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int g = lane >> 4, L = lane & 15;
+  lds_u8* const dot = smem + STAGES * 2 * TILE_BYTES + wave * DO_BYTES + lane * 16;
+
+  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
+  const int b = tc.head / p.Hq;
+  const int h = tc.head - b * p.Hq;
+  const int hk = h / (p.Hq / p.Hkv);
+  const size_t qh = (size_t)(b * p.Hq + h) * N;
+  const __bf16* kg = (const __bf16*)p.k + (size_t)(b * p.Hkv + hk) * N * D;
+  const __bf16* vg = (const __bf16*)p.v + (size_t)(b * p.Hkv + hk) * N * D;
+
+  const int q0 = tc.tile * BM;
+  const int qw0 = q0 + wave * QPW;
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int n_kv = (kv_end + BN - 1) / BN;
+  const int n_ch = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
+  const int first_mask = min(n_ch, CAUSAL ? min(qw0 / 32, N / 32) : N / 32);
+
+  auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
+    const int kv0 = t * BN;
+    const uint32_t dst = lds_address(smem) + (t % STAGES) * 2 * TILE_BYTES;
+#pragma unroll
+    for (int c = 0; c < COPIES_PER_WAVE; ++c) {
+      const int piece = wave * COPIES_PER_WAVE + c;
+      const int prow = piece * ROWS_PER_COPY + lane / CH;
+      const int lch = (lane % CH) ^ Swz::f(prow);  // logical chunk stored at this lane's physical chunk
+      const int grow = min(kv0 + prow, N - 1);    // rows past the end: any valid row, masked later
+      const uint32_t src = (uint32_t)(grow * D + lch * 8) * 2;
+      copy16_global_to_lds_async(kg, src, dst + piece * 1024);
+      copy16_global_to_lds_async(vg, src, dst + TILE_BYTES + piece * 1024);
+    }
+  };
+  for (int t = 0; t < STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
+
+  // Q^T fragments (B operand) in registers, dO^T fragments in this wave's LDS
+  // region (lane-major, conflict free), the row's lse (log2 units) and D
+  bf16x8 qf[QB][DC];
+  float lse2[QB], dl[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = min(qw0 + qb * 16 + L, N - 1);
+    const u32x4* qs = (const u32x4*)((const __bf16*)p.q + (qh + row) * D + g * 8);
+    const u32x4* ds = (const u32x4*)((const __bf16*)p.dout + (qh + row) * D + g * 8);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      qf[qb][dc] = __builtin_bit_cast(bf16x8, qs[dc * 4]);
+      *(FA_LDS u32x4*)(dot + (qb * DC + dc) * 1024) = ds[dc * 4];
+    }
+    lse2[qb] = p.lse[qh + row] * 1.4426950408889634f;
+    dl[qb] = p.delta[qh + row];
+  }
+  f32x4 acc[DB][QB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c = p.scale_log2;
+  // key k of a chunk is visible to this lane's query iff k <= lim; on masked
+  // chunks the test is hb * 16 + r <= lim - (chunk start + 4g)
+  int lim[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lim[qb] = (CAUSAL ? min(qw0 + qb * 16 + L, N - 1) : N - 1) - 4 * g;
+
+  // lane parts of the LDS fragment offsets
+  int r_off[DC];  // row L of a 16-row block, chunk dc*4 + g
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
+  int t_off[DB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
+  {
+    const int trow = 4 * g + (L >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      t_off[db] = trow * RB + (((2 * db + ((L & 3) >> 1)) ^ Swz::f(trow)) << 4) + 8 * (L & 1);
+  }
+
+  // One 32-key chunk (K rows at kt, V rows at kt + TILE_BYTES, chunk index ch).
+  auto chunk = [&](const lds_u8* kt, int ch, auto mask) __attribute__((always_inline)) {
+    const lds_u8* vt = kt + TILE_BYTES;
+    // S^T = K Q^T and dP^T = V dO^T, one 16-key half at a time, each half
+    // turned into dS^T = P^T o (dP^T - D) and packed to bf16 right away
+    u32x2 half_pk[2][QB];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      f32x4 s[QB], dp[QB];
+      {
+        bf16x8 kf[DC], vf[DC], df[QB][DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          kf[dc] = lds_read_b128(kt + hb * 16 * RB + r_off[dc]);
+          vf[dc] = lds_read_b128(vt + hb * 16 * RB + r_off[dc]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) df[qb][dc] = lds_read_b128(dot + (qb * DC + dc) * 1024);
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            s[qb] = mfma_bf16_16x16x32(kf[dc], qf[qb][dc], s[qb]);
+            dp[qb] = mfma_bf16_16x16x32(vf[dc], df[qb][dc], dp[qb]);
+          }
+        __builtin_amdgcn_s_setprio(0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = s[qb][r];
+          if (decltype(mask)::value) x = (hb * 16 + r <= lim[qb] - ch * 32) ? x : kNegInf;
+          e[r] = exp2_fast(fmaf(x, c, -lse2[qb])) * (dp[qb][r] - dl[qb]);
+        }
+        half_pk[hb][qb] = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dS^T as the B operand of dQ^T += K^T dS^T: element e < 4 -> key 4g + e,
+    // e >= 4 -> key 16 + 4g + e - 4 of the chunk
+    bf16x8 dsf[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      dsf[qb] = __builtin_bit_cast(bf16x8, u32x4{half_pk[0][qb][0], half_pk[0][qb][1], half_pk[1][qb][0],
+                                                half_pk[1][qb][1]});
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo = lds_read_tr16_b64(kt + t_off[db]);
+      const i16x4 hi = lds_read_tr16_b64(kt + 16 * RB + t_off[db]);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma_bf16_16x16x32(ka, dsf[qb], acc[db][qb]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // key loop: tile t is published by the barrier at its start; at that point
+  // every wave is done with tile t-1, whose stage receives tile t+STAGES-1.
+  // (the stage base is a run-time value, so the address arithmetic of the
+  // three stages is not hoisted into registers of its own)
+  // Two loops: tiles before t_mask need no mask in any wave (straight-line
+  // bodies), the rest (the workgroup's diagonal and the end of the sequence)
+  // take the masked path per wave.
+  int stage = 0;
+  auto begin_tile = [&](int t) __attribute__((always_inline)) {
+    if (t + STAGES - 2 < n_kv) {
+      wait_vmcnt_le<(STAGES - 2) * OPS>();  // tile t landed; tiles up to t+STAGES-2 may fly
+    } else {
+      wait_vmcnt0();
+    }
+    __syncthreads();
+    if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
+    const lds_u8* kt = smem + uniform(stage * 2 * TILE_BYTES);
+    stage = (stage == STAGES - 1) ? 0 : stage + 1;
+    return kt;
+  };
+  const int t_mask = min(n_kv, (CAUSAL ? min(q0, N) : N) / BN);
+  int t = 0;
+  for (; t < t_mask; ++t) {
+    const lds_u8* kt = begin_tile(t);
+    chunk(kt, 2 * t, std::false_type{});
+    chunk(kt + 32 * RB, 2 * t + 1, std::false_type{});
+  }
+  for (; t < n_kv; ++t) {
+    const lds_u8* kt = begin_tile(t);
+    const int ch0 = 2 * t;
+    if (ch0 < n_ch) chunk(kt, ch0, std::true_type{});
+    if (ch0 + 1 < n_ch) chunk(kt + 32 * RB, ch0 + 1, std::true_type{});
+  }
+
+  // dQ = scale * dQ^T: lane holds query L + 16 qb, d = 16 db + 4 g + r
+  __bf16* dqg = (__bf16*)p.dq + qh * D;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 16 + L;
+    if (row < N) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 v4 = acc[db][qb] * p.scale;
+        *(u32x2*)(dqg + (size_t)row * D + db * 16 + 4 * g) =
+            u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launch
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipEvent_t* ev) {
@@ -355,17 +536,16 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     (const __bf16*)p.o, (const __bf16*)p.dout, p.delta, p.dq_acc, rows);
+                     (const __bf16*)p.o, (const __bf16*)p.dout, p.delta, rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + 127) / 128;
-  hipLaunchKernelGGL((fa_bwd_main_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(256), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  const long long n4 = rows * D / 4;
-  hipLaunchKernelGGL(fa_bwd_dq_convert_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p.dq_acc,
-                     (__bf16*)p.dq, p.scale, n4);
+  p.n_tiles = (p.N + 255) / 256;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;

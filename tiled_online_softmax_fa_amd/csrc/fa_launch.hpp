@@ -28,7 +28,6 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;   // [B, Hq, N] workspace: D_i = sum_c dout_ic o_ic
-  float* dq_acc;  // [B, Hq, N, d] workspace: fp32 dq accumulator
   int B, Hq, Hkv, N;
   float scale;
   float scale_log2;
