@@ -13,15 +13,11 @@
 // Three kernels on the caller's stream:
 //   1. row term D (fp32);
 //   2. dK, dV: one workgroup per (key tile of 128 keys, batch * key/value
-//      head): K, V of the tile stay in registers, each of the 4 waves owns 32
-//      keys and accumulates their dK^T, dV^T; query tiles of 64 rows (Q, dO)
-//      stream through LDS (the tiled backward of the page "Flash Attention-2"
-//      (deepschool.ru), "Улучшение backward pass", and blogweb.cn section 5).
-//      S = Q K^T is computed with keys on the accumulator's columns, so P and
-//      dS come out of the MFMA in the B-operand layout of dV^T += dO^T P and
-//      dK^T += Q^T dS, whose dO^T / Q^T fragments are transposing LDS reads.
-//      For grouped heads the query loop covers every query head of the
-//      group, so dK and dV are summed in registers;
+//      head); query tiles of 64 rows (Q, dO, lse, D) stream through LDS (the
+//      tiled backward of the page "Flash Attention-2" (deepschool.ru),
+//      "Улучшение backward pass", and blogweb.cn section 5). Two waves per
+//      32-key slice split the work: one computes P and dV, the other dP, dS
+//      and dK (details at the kernel);
 //   3. dQ: one workgroup per (query tile, batch * query head), built like
 //      the forward kernel: Q and dO stay in registers and K, V tiles stream
 //      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
@@ -58,236 +54,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const __bf16* __restric
   if (row < rows && sub == 0) delta[row] = s;
 }
 
-// ------------------------------------------------------------------ kernel 2: dK, dV
-template <int D>
-struct TileSwizzle {  // 16-byte chunk XOR swizzle of a row-major [rows][D] bf16 tile
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kChunks16 = kRowBytes / 16;
-  static constexpr int kRowsPer256 = 256 / kRowBytes;
-  __device__ static __forceinline__ int swz(int row) { return (row / kRowsPer256) % kChunks16; }
-  // byte offset of element (row, col) for an 8-byte aligned col group
-  __device__ static __forceinline__ int offset(int row, int col) {
-    const int chunk = (col >> 3) ^ swz(row);
-    return row * kRowBytes + chunk * 16 + (col & 7) * 2;
-  }
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = 4, KPW = 32, BNK = NW * KPW;  // 128 keys per workgroup
-  constexpr int BMQ = 64;                          // query rows per step
-  constexpr int QB = BMQ / 16, KB = KPW / 16, QC = BMQ / 32;
-  constexpr int DC = D / 32, DB = D / 16;
-  constexpr int QTILE_BYTES = BMQ * D * 2;
-  constexpr int COPIES_PER_WAVE = QTILE_BYTES / 1024 / NW;
-  constexpr int ROWS_PER_COPY = 1024 / (2 * D);
-  constexpr int CH = 2 * D / 16;
-  using Swz = TileSwizzle<D>;
-  static_assert(COPIES_PER_WAVE >= 1, "tile copy split");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char q_stage0[QTILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_stage0[QTILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char q_stage1[QTILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_stage1[QTILE_BYTES];
-
-  const int N = p.N;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int g = lane >> 4, L = lane & 15;
-  const int G = p.Hq / p.Hkv;
-
-  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
-  const int b = tc.head / p.Hkv;
-  const int hk = tc.head - b * p.Hkv;
-  const int kv0 = tc.tile * BNK;
-  const int kw0 = kv0 + wave * KPW;  // this wave's first key
-  const size_t kv_head = (size_t)(b * p.Hkv + hk) * N;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + kv_head * D;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + kv_head * D;
-
-  // K^T, V^T fragments of this wave's keys into registers (B operands of
-  // S = Q K^T and dP = dO V^T).
-  bf16x8 kf[KB][DC], vf[KB][DC];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int row = min(kw0 + kb * 16 + L, N - 1);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      kf[kb][dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(kg + (size_t)row * D + dc * 32 + g * 8));
-      vf[kb][dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vg + (size_t)row * D + dc * 32 + g * 8));
-    }
-  }
-
-  f32x4 dv_acc[DB][KB], dk_acc[DB][KB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      dv_acc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dk_acc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  const int nq = (N + BMQ - 1) / BMQ;
-  const int i_begin = CAUSAL ? (kv0 / BMQ) : 0;  // first query tile with a visible key
-  const int steps_per_head = nq - i_begin;
-  const int n_steps = steps_per_head * G;
-  const float c = p.scale_log2;
-  constexpr float kLog2e = 1.4426950408889634f;
-
-  auto step_coords = [&](int s, int& h, int& i) __attribute__((always_inline)) {
-    const int gi = s / steps_per_head;
-    h = hk * G + gi;
-    i = i_begin + (s - gi * steps_per_head);
-  };
-  auto issue_copy = [&](int s, lds_u8* qdst, lds_u8* ddst) __attribute__((always_inline)) {
-    int h, i;
-    step_coords(s, h, i);
-    const size_t qh = (size_t)(b * p.Hq + h) * N;
-    const __bf16* qsrc = (const __bf16*)p.q + qh * D;
-    const __bf16* dsrc = (const __bf16*)p.dout + qh * D;
-#pragma unroll
-    for (int cp = 0; cp < COPIES_PER_WAVE; ++cp) {
-      const int piece = wave * COPIES_PER_WAVE + cp;
-      const int prow = piece * ROWS_PER_COPY + lane / CH;
-      const int pch = lane % CH;
-      const int grow = min(i * BMQ + prow, N - 1);
-      const int lch = pch ^ Swz::swz(prow);
-      copy16_global_to_lds(qsrc + (size_t)grow * D + lch * 8, qdst + piece * 1024);
-      copy16_global_to_lds(dsrc + (size_t)grow * D + lch * 8, ddst + piece * 1024);
-    }
-  };
-
-  auto step = [&](auto stage, int s) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    lds_u8* qt = (lds_u8*)(ST == 0 ? q_stage0 : q_stage1);
-    lds_u8* dt = (lds_u8*)(ST == 0 ? do_stage0 : do_stage1);
-    wait_vmcnt0();
-    __syncthreads();  // tile s landed; every wave is done with tile s-1
-    if (s + 1 < n_steps) issue_copy(s + 1, (lds_u8*)(ST == 0 ? q_stage1 : q_stage0),
-                                    (lds_u8*)(ST == 0 ? do_stage1 : do_stage0));
-    int h, i;
-    step_coords(s, h, i);
-    const int q0 = i * BMQ;
-    const size_t qh = (size_t)(b * p.Hq + h) * N;
-
-    // ---- S = Q K^T and dP = dO V^T: blocks of 16 queries x 16 keys (keys on columns)
-    f32x4 sacc[QB][KB], pacc[QB][KB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = qb * 16 + L;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const int off = Swz::offset(row, dc * 32 + g * 8);
-        const bf16x8 qa = lds_read_b128(qt + off);
-        const bf16x8 da = lds_read_b128(dt + off);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          sacc[qb][kb] = mfma_bf16_16x16x32(qa, kf[kb][dc], sacc[qb][kb]);
-          pacc[qb][kb] = mfma_bf16_16x16x32(da, vf[kb][dc], pacc[qb][kb]);
-        }
-      }
-    }
-
-    // ---- P = 2^(c S - lse log2 e) (0 where masked), dS = P (dP - D)
-    const bool need_mask = (q0 + BMQ > N) || (kw0 + KPW > N) || (CAUSAL && kw0 + KPW - 1 > q0);
-    bf16x8 pfr[QC][KB], dsfr[QC][KB];
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      u32x2 pp[2][KB], dd[2][KB];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qb = 2 * qc + half;
-        const int qrow = q0 + qb * 16 + 4 * g;  // this lane's queries: qrow + r, r = 0..3
-        float lse2[4], dl[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = min(qrow + r, N - 1);
-          lse2[r] = p.lse[qh + qq] * kLog2e;
-          dl[r] = p.delta[qh + qq];
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float pr = exp2_fast(fmaf(sacc[qb][kb][r], c, -lse2[r]));
-            if (need_mask) {
-              const int key = kw0 + kb * 16 + L, qi = qrow + r;
-              const bool visible = key < N && qi < N && (!CAUSAL || key <= qi);
-              pr = visible ? pr : 0.f;
-            }
-            pv[r] = pr;
-            dsv[r] = pr * (pacc[qb][kb][r] - dl[r]);
-          }
-          pp[half][kb] = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-          dd[half][kb] = u32x2{pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3])};
-        }
-      }
-      // B-operand packing: elements 0..3 <- query block 2qc (rows 4g + e), 4..7 <- block 2qc + 1
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        pfr[qc][kb] = __builtin_bit_cast(bf16x8, u32x4{pp[0][kb][0], pp[0][kb][1], pp[1][kb][0], pp[1][kb][1]});
-        dsfr[qc][kb] = __builtin_bit_cast(bf16x8, u32x4{dd[0][kb][0], dd[0][kb][1], dd[1][kb][0], dd[1][kb][1]});
-      }
-    }
-
-    // ---- dV^T += dO^T P, dK^T += Q^T dS (A operands: transposing reads of the dO / Q tiles)
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      const int r0 = qc * 32 + 4 * g + (L >> 2), r1 = r0 + 16;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = db * 16 + 4 * (L & 3);
-        const i16x4 d_lo = lds_read_tr16_b64(dt + Swz::offset(r0, col));
-        const i16x4 d_hi = lds_read_tr16_b64(dt + Swz::offset(r1, col));
-        const i16x4 q_lo = lds_read_tr16_b64(qt + Swz::offset(r0, col));
-        const i16x4 q_hi = lds_read_tr16_b64(qt + Swz::offset(r1, col));
-        const bf16x8 dTa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d_lo, d_hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 qTa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q_lo, q_hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          dv_acc[db][kb] = mfma_bf16_16x16x32(dTa, pfr[qc][kb], dv_acc[db][kb]);
-          dk_acc[db][kb] = mfma_bf16_16x16x32(qTa, dsfr[qc][kb], dk_acc[db][kb]);
-        }
-      }
-    }
-
-  };
-
-  if (n_steps > 0) issue_copy(0, (lds_u8*)q_stage0, (lds_u8*)do_stage0);
-  for (int s = 0; s < n_steps; s += 2) {
-    step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < n_steps) step(std::integral_constant<int, 1>{}, s + 1);
-  }
-
-  // ---- dK = scale * dK^T acc, dV = dV^T acc (lane: key column, rows d = 16db + 4g + r)
-  __bf16* dkg = (__bf16*)p.dk + kv_head * D;
-  __bf16* dvg = (__bf16*)p.dv + kv_head * D;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw0 + kb * 16 + L;
-    if (key < N) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 k4 = dk_acc[db][kb] * p.scale;
-        const f32x4 v4 = dv_acc[db][kb];
-        u32x2 kp = {pack_bf16x2(k4[0], k4[1]), pack_bf16x2(k4[2], k4[3])};
-        u32x2 vp = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-        *(u32x2*)(dkg + (size_t)key * D + db * 16 + 4 * g) = kp;
-        *(u32x2*)(dvg + (size_t)key * D + db * 16 + 4 * g) = vp;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ kernel 3: dQ
+// ------------------------------------------------------------------ LDS layout shared by kernels 2 and 3
 //
 // Tiles here are read both row-wise (16-byte reads of one row's chunk) and
 // transposed (ds_read_b64_tr_b16), so the 16-byte chunk c of row r is stored
@@ -306,6 +73,307 @@ struct DualSwizzle {
   }
 };
 
+// ------------------------------------------------------------------ kernel 2: dK, dV
+//
+// One workgroup of 8 waves per (key tile of 128 keys, batch * key/value
+// head). The waves form 4 pairs; pair p owns keys kv0 + 32p .. +31 and its two
+// waves share one SIMD (waves p and p + 4):
+//   wave A (p):     S = Q K^T, P = 2^(c S - lse log2 e) (masked), dV^T += dO^T P
+//   wave B (p + 4): dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
+// so each wave keeps one of K^T / V^T and one accumulator in registers.
+// Keys sit on the accumulator's columns: P and dS come out of the MFMA in
+// the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A
+// operands dO^T, Q^T are transposing LDS reads of the row-major tiles.
+// Wave A hands P (bf16) to wave B through LDS; wave B runs one query tile
+// behind, so one workgroup barrier per tile publishes both the next Q/dO
+// tile and the previous tile's P. Query tiles of 64 rows (Q, dO, lse, D)
+// stream through a 3-stage ring of asynchronous copies: at step s tile s is
+// read by A, tile s-1 by B, and the stage of tile s-2 receives tile s+1.
+// For grouped heads the sequence of tiles covers every query head of the
+// group, so dK and dV are summed in registers.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NP = 4, KPW = 32, BNK = NP * KPW;  // 128 keys per workgroup
+  constexpr int BMQ = 64, STAGES = 3;             // query rows per tile
+  constexpr int KB = KPW / 16, QB = 2, DC = D / 32, DB = D / 16;
+  constexpr int RB = 2 * D;
+  constexpr int QT_BYTES = BMQ * RB;                       // one Q (or dO) tile
+  constexpr int LSE_OFF = 2 * QT_BYTES, DEL_OFF = LSE_OFF + BMQ * 4;
+  constexpr int STAGE_BYTES = 2 * QT_BYTES + 2 * BMQ * 4;  // Q, dO, lse, D
+  constexpr int PIECES = 2 * QT_BYTES / 1024;              // 1 KiB copies per tile (Q and dO)
+  constexpr int PIECES_PER_WAVE = PIECES / 8;
+  constexpr int ROWS_PER_PIECE = 1024 / RB;
+  constexpr int CH = RB / 16;
+  constexpr int P_BYTES = 2 * 2 * 64 * 16;                 // one pair's P of one tile: 2 chunks x 2 halves
+  using Swz = DualSwizzle<D>;
+  static_assert(PIECES % 8 == 0 && PIECES_PER_WAVE >= 1, "copy split");
+  static_assert(STAGE_BYTES % 256 == 0, "stage alignment");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * STAGE_BYTES + 2 * NP * P_BYTES];
+  lds_u8* const smem = (lds_u8*)smem_raw;
+
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int role = wave >> 2, pair = wave & 3;
+  const int g = lane >> 4, L = lane & 15;
+  const int G = p.Hq / p.Hkv;
+
+  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
+  const int b = tc.head / p.Hkv;
+  const int hk = tc.head - b * p.Hkv;
+  const int kv0 = tc.tile * BNK;
+  const int kw0 = kv0 + pair * KPW;  // this pair's first key
+  const size_t kv_head = (size_t)(b * p.Hkv + hk) * N;
+
+  const int nq = (N + BMQ - 1) / BMQ;
+  const int t_first = CAUSAL ? kv0 / BMQ : 0;  // first query tile with a visible key
+  const int per_head = nq - t_first;
+  const int n_seq = per_head * G;             // tiles in the sequence (all heads of the group)
+
+  // ---- copies of sequence tile j (query head hk*G + j / per_head, query tile
+  // t_first + j % per_head) into stage j % STAGES
+  auto issue_tile_copy = [&](int j) __attribute__((always_inline)) {
+    const int gi = j / per_head;
+    const int tq = t_first + (j - gi * per_head);
+    const size_t qh = (size_t)(b * p.Hq + hk * G + gi) * N;
+    const uint32_t dst = lds_address(smem) + (j % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int c = 0; c < PIECES_PER_WAVE; ++c) {
+      const int piece = wave * PIECES_PER_WAVE + c;
+      const int which = piece / (PIECES / 2);  // 0: Q, 1: dO
+      const int pp = piece - which * (PIECES / 2);
+      const int prow = pp * ROWS_PER_PIECE + lane / CH;
+      const int lch = (lane % CH) ^ Swz::f(prow);
+      const int grow = min(tq * BMQ + prow, N - 1);  // rows past the end: any valid row, masked later
+      const void* base = which ? (const void*)((const __bf16*)p.dout + qh * D) : (const void*)((const __bf16*)p.q + qh * D);
+      copy16_global_to_lds_async(base, (uint32_t)(grow * D + lch * 8) * 2, dst + which * QT_BYTES + pp * 1024);
+    }
+    // lse (waves 0-3) or D (waves 4-7): 16 rows per wave, one dword per lane
+    if (lane < 16) {
+      const int row = min(tq * BMQ + 16 * pair + lane, N - 1);
+      const float* src = (role == 0 ? p.lse : p.delta) + qh;
+      copy4_global_to_lds_async(src, (uint32_t)row * 4, dst + (role == 0 ? LSE_OFF : DEL_OFF) + 64 * pair);
+    }
+  };
+  constexpr int OPS = PIECES_PER_WAVE + 1;  // copy instructions per wave per tile
+  (void)OPS;
+
+  if (n_seq > 0) issue_tile_copy(0);
+
+  // K^T (wave A) or V^T (wave B) fragments of the pair's keys: B operands
+  // (column = key kw0 + 16 kb + L, k = d)
+  bf16x8 kvf[KB][DC];
+  {
+    const __bf16* src = (const __bf16*)(role == 0 ? p.k : p.v) + kv_head * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int row = min(kw0 + kb * 16 + L, N - 1);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        kvf[kb][dc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + (size_t)row * D + dc * 32 + g * 8));
+    }
+  }
+  f32x4 acc[DB][KB];  // dV^T (wave A) or dK^T (wave B): rows d, columns keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const float c = p.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  int r_off[DC];  // row-wise read: row L of a 16-row block, chunk dc*4 + g
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
+  int t_off[DB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
+  {
+    const int trow = 4 * g + (L >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      t_off[db] = trow * RB + (((2 * db + ((L & 3) >> 1)) ^ Swz::f(trow)) << 4) + 8 * (L & 1);
+  }
+  // P buffer of this pair: [tile parity][chunk][half][lane] x 16 bytes
+  lds_u8* const pbuf = smem + STAGES * STAGE_BYTES + pair * 2 * P_BYTES + lane * 16;
+
+  // ---- one step: wait for tile s, publish it (and P of tile s-1), refill
+  auto begin_step = [&](int s) __attribute__((always_inline)) {
+    wait_vmcnt0();  // tile s landed (the only copies in flight)
+    __syncthreads();
+    if (s + 1 < n_seq) issue_tile_copy(s + 1);
+  };
+
+  // mask for wave A: key kw0 + 16 kb + L is visible to query q iff
+  // lo[kb] <= q - 4g and q - 4g <= hi (q = the lane's query 4g + r of a block)
+  int lo[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) lo[kb] = (CAUSAL ? kw0 + kb * 16 + L : 0) - 4 * g;
+  const int hi = N - 1 - 4 * g;
+
+  // wave A, query chunk cc of tile j (query rows q0 + 32 cc ..)
+  auto chunk_a = [&](const lds_u8* st, int q0, int cc, lds_u8* pb, auto mask) __attribute__((always_inline)) {
+    const lds_u8* qt = st;
+    const lds_u8* dt = st + QT_BYTES;
+    f32x4 s[QB][KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bf16x8 a = lds_read_b128(qt + (cc * 32 + qb * 16) * RB + r_off[dc]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], s[qb][kb]);
+      }
+    __builtin_amdgcn_s_setprio(0);
+    // P = 2^(c S - lse log2 e); B-operand packing: e < 4 -> query block 0
+    // (rows 4g + e), e >= 4 -> block 1 (rows 16 + 4g + e - 4)
+    u32x4 pw[KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const f32x4 l4 = *(const FA_LDS f32x4*)(st + LSE_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = s[qb][kb][r];
+          if (decltype(mask)::value) {
+            const int qq = q0 + cc * 32 + qb * 16 + r;  // query - 4g
+            x = (qq >= lo[kb] && qq <= hi) ? x : kNegInf;
+          }
+          e[r] = exp2_fast(fmaf(x, c, -l4[r] * kLog2e));
+        }
+        pw[kb][2 * qb] = pack_bf16x2(e[0], e[1]);
+        pw[kb][2 * qb + 1] = pack_bf16x2(e[2], e[3]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) *(FA_LDS u32x4*)(pb + (cc * 2 + kb) * 1024) = pw[kb];
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo4 = lds_read_tr16_b64(dt + cc * 32 * RB + t_off[db]);
+      const i16x4 hi4 = lds_read_tr16_b64(dt + (cc * 32 + 16) * RB + t_off[db]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, pw[kb]), acc[db][kb]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // wave B, query chunk cc of the previous tile
+  auto chunk_b = [&](const lds_u8* st, int cc, const lds_u8* pb) __attribute__((always_inline)) {
+    const lds_u8* qt = st;
+    const lds_u8* dt = st + QT_BYTES;
+    f32x4 dp[QB][KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bf16x8 a = lds_read_b128(dt + (cc * 32 + qb * 16) * RB + r_off[dc]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], dp[qb][kb]);
+      }
+    __builtin_amdgcn_s_setprio(0);
+    u32x4 dw[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 pw = *(const FA_LDS u32x4*)(pb + (cc * 2 + kb) * 1024);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const f32x4 d4 = *(const FA_LDS f32x4*)(st + DEL_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
+        float e[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t w = pw[2 * qb + h2];
+          const float p0 = __builtin_bit_cast(float, w << 16);
+          const float p1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
+          e[2 * h2] = p0 * (dp[qb][kb][2 * h2] - d4[2 * h2]);
+          e[2 * h2 + 1] = p1 * (dp[qb][kb][2 * h2 + 1] - d4[2 * h2 + 1]);
+        }
+        dw[kb][2 * qb] = pack_bf16x2(e[0], e[1]);
+        dw[kb][2 * qb + 1] = pack_bf16x2(e[2], e[3]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo4 = lds_read_tr16_b64(qt + cc * 32 * RB + t_off[db]);
+      const i16x4 hi4 = lds_read_tr16_b64(qt + (cc * 32 + 16) * RB + t_off[db]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, dw[kb]), acc[db][kb]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto stage_of = [&](int j) __attribute__((always_inline)) { return smem + uniform((j % STAGES) * STAGE_BYTES); };
+  auto pbuf_of = [&](int j) __attribute__((always_inline)) { return pbuf + uniform((j & 1) * P_BYTES); };
+
+  if (role == 0) {
+    // wave A: steps 0 .. n_seq-1 process tile s; a last step keeps the
+    // barrier count equal to wave B's. Per head: the first two tiles (the
+    // diagonal under causal) and a partial last tile take the masked path.
+    const int t_clean0 = CAUSAL ? t_first + 2 : 0;  // first tile no wave of the workgroup masks
+    const int t_clean1 = N / BMQ;                   // end of the full tiles
+    int s = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      int tq = t_first;
+      for (; tq < min(t_clean0, nq); ++tq, ++s) {
+        begin_step(s);
+        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::true_type{});
+        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::true_type{});
+      }
+      for (; tq < t_clean1; ++tq, ++s) {
+        begin_step(s);
+        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::false_type{});
+        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::false_type{});
+      }
+      for (; tq < nq; ++tq, ++s) {
+        begin_step(s);
+        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::true_type{});
+        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::true_type{});
+      }
+    }
+    if (n_seq > 0) begin_step(n_seq);
+  } else {
+    // wave B: step s processes tile s-1
+    if (n_seq > 0) begin_step(0);
+    for (int s = 1; s <= n_seq; ++s) {
+      begin_step(s);
+      chunk_b(stage_of(s - 1), 0, pbuf_of(s - 1));
+      chunk_b(stage_of(s - 1), 1, pbuf_of(s - 1));
+    }
+  }
+
+  // ---- dV = dV^T acc (wave A), dK = scale * dK^T acc (wave B); lane: key
+  // column, rows d = 16 db + 4 g + r
+  __bf16* out = (__bf16*)(role == 0 ? p.dv : p.dk) + kv_head * D;
+  const float osc = role == 0 ? 1.0f : p.scale;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + kb * 16 + L;
+    if (key < N) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 v4 = acc[db][kb] * osc;
+        *(u32x2*)(out + (size_t)key * D + db * 16 + 4 * g) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernel 3: dQ
+//
 // One workgroup of 8 waves per (query tile of 256 rows, batch * query head);
 // each wave owns 32 query rows. Per 32-key chunk, with keys on the
 // accumulator rows and queries on its columns (as in the forward kernel):
@@ -540,7 +608,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + 127) / 128;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(512), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;

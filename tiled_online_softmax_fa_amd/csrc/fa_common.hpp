@@ -85,6 +85,20 @@ __device__ __forceinline__ void copy16_global_to_lds_async(const void* base, uin
       : "memory");
 }
 
+// 4-byte variant: lane i writes lds_addr + 4 i.
+__device__ __forceinline__ void copy4_global_to_lds_async(const void* base, uint32_t voffset, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voffset), "s"(lds_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_u8* p) {
