@@ -185,10 +185,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
   static_assert(D == 64 || 16 % Swz::kRowsPer256 == 0, "swizzle period");
 
-  // K fragments (A operand of S^T) of chunk cc (0..CPT-1) of the tile in stage ST
-  auto read_k = [&](auto st, int cc, bf16x8 (&kf)[2][DC]) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    const lds_u8* kt = smem + ST * 2 * TILE_BYTES;
+  // K fragments (A operand of S^T) of chunk cc (0..CPT-1) of the K tile at kt
+  auto read_k = [&](const lds_u8* kt, int cc, bf16x8 (&kf)[2][DC]) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -197,9 +195,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   };
   // V^T fragments (A operand of O^T += V^T P^T): rows d = 16 db + lane % 16,
   // element e < 4 -> key 4g + e, e >= 4 -> key 16 + 4g + e - 4 of the chunk
-  auto read_v = [&](auto st, int cc, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    const lds_u8* vt = smem + ST * 2 * TILE_BYTES + TILE_BYTES + cc * 32 * (2 * D);
+  auto read_v = [&](const lds_u8* kt, int cc, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+    const lds_u8* vt = kt + TILE_BYTES + cc * 32 * (2 * D);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const i16x4 lo = lds_read_tr16_b64(vt + v_off[db]);
@@ -293,10 +290,10 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // S^T of the chunk about to be exponentiated (masked, maximum folded in)
   f32x4 s_cur[2][QB];
 
-  // S^T of chunk ch (in stage ST, position cc), masked when MASK, and the reference update.
-  auto scores = [&](auto st, int cc, int ch, auto mask) __attribute__((always_inline)) {
+  // S^T of chunk ch (K tile at kt, position cc), masked when MASK, and the reference update.
+  auto scores = [&](const lds_u8* kt, int cc, int ch, auto mask) __attribute__((always_inline)) {
     bf16x8 kf[2][DC];
-    read_k(st, cc, kf);
+    read_k(kt, cc, kf);
     compute_s(kf, s_cur);
     if (decltype(mask)::value) apply_mask(ch, s_cur);
     float tmax[QB];
@@ -305,30 +302,37 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   };
 
   // Chunk ch (S^T in s_cur, reference current): exponentials and O^T += V^T P^T
-  // of ch, then S^T and the maximum of chunk ch+1. In the steady state (chunk
-  // ch+1 needs no mask) all of it up to the vote on ch+1 is one straight-line
-  // block, so the scheduler overlaps the exponentials of ch with the matrix
-  // work of ch+1. ST/CC: stage and position of ch; STN/CCN: those of ch+1.
-  auto chunk_step = [&](auto st, auto cc, auto stn, auto ccn, int ch) __attribute__((always_inline)) {
+  // of ch, then S^T and the maximum of chunk ch+1 (K tile at ktn, position
+  // ccn). Up to the vote on ch+1 this is one straight-line block, so the
+  // scheduler overlaps the exponentials of ch with the matrix work of ch+1.
+  auto chunk_step = [&](const lds_u8* kt, int cc, const lds_u8* ktn, int ccn, int ch, auto mask)
+                        __attribute__((always_inline)) {
     bf16x8 vf[DB], pf[QB];
-    if (ch + 1 < first_mask) {
-      read_v(st, cc, vf);
-      exponentiate(s_cur, pf);
-      accumulate_pv(vf, pf);
-      scores(stn, ccn, ch + 1, std::false_type{});
-    } else {
-      read_v(st, cc, vf);
-      exponentiate(s_cur, pf);
-      accumulate_pv(vf, pf);
-      if (ch + 1 < n_ch) scores(stn, ccn, ch + 1, std::true_type{});
-    }
+    read_v(kt, cc, vf);
+    exponentiate(s_cur, pf);
+    accumulate_pv(vf, pf);
+    if (!decltype(mask)::value || ch + 1 < n_ch) scores(ktn, ccn, ch + 1, mask);
   };
 
   // ---- key loop: tiles in workgroup lock-step, chunks per wave. The last
   // chunk of tile t reads K of tile t+1, so tile t+1 is published by the
   // barrier just before it; at that point every wave is done with tile t-1,
-  // whose stage receives tile t+STAGES-1. The loop is unrolled over the
-  // STAGES stages so that every LDS address has a constant stage part.
+  // whose stage receives tile t+STAGES-1. Tiles before t_steady need no mask
+  // in any wave (this tile's chunks and the first chunk of the next): they
+  // run in a loop of their own with branch-free bodies; the diagonal and the
+  // end of the sequence take the masked path. Stage bases are run-time values.
+  auto stage_base = [&](int t) __attribute__((always_inline)) {
+    return smem + uniform((t % STAGES) * 2 * TILE_BYTES);
+  };
+  auto publish_next = [&](int t) __attribute__((always_inline)) {
+    if (t + STAGES - 2 < n_kv) {
+      wait_vmcnt_le<(STAGES - 3) * OPS>();  // tile t+1 landed; tiles up to t+STAGES-2 may fly
+    } else {
+      wait_vmcnt0();
+    }
+    __syncthreads();
+    if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
+  };
   if (n_kv > 0) {
     if (n_kv >= STAGES - 1) {
       wait_vmcnt_le<(STAGES - 2) * OPS>();  // tile 0 landed; tiles 1..STAGES-2 may still fly
@@ -338,41 +342,27 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     if (n_ch > 0) {
       if (first_mask > 0) {
-        scores(std::integral_constant<int, 0>{}, 0, 0, std::false_type{});
+        scores(smem, 0, 0, std::false_type{});
       } else {
-        scores(std::integral_constant<int, 0>{}, 0, 0, std::true_type{});
+        scores(smem, 0, 0, std::true_type{});
       }
     }
   }
-  auto tile = [&](auto st, int t) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    constexpr int STN = (ST + 1) % STAGES;
-    static_assert(CPT == 2, "two 32-key chunks per tile");
-    // chunk 0 of tile t: next chunk in the same tile
-    if (2 * t < n_ch)
-      chunk_step(st, std::integral_constant<int, 0>{}, st, std::integral_constant<int, 1>{}, 2 * t);
-    // chunk 1 of tile t reads K of tile t+1: publish it first
-    if (t + 1 < n_kv) {
-      if (t + STAGES - 2 < n_kv) {
-        wait_vmcnt_le<(STAGES - 3) * OPS>();  // tile t+1 landed; tiles up to t+STAGES-2 may fly
-      } else {
-        wait_vmcnt0();
-      }
-      __syncthreads();
-      if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
-    }
-    if (2 * t + 1 < n_ch)
-      chunk_step(st, std::integral_constant<int, 1>{}, std::integral_constant<int, STN>{},
-                 std::integral_constant<int, 0>{}, 2 * t + 1);
-  };
-  for (int t0 = 0; t0 < n_kv; t0 += STAGES) {
-    tile(std::integral_constant<int, 0>{}, t0);
-    if (t0 + 1 < n_kv) tile(std::integral_constant<int, 1>{}, t0 + 1);
-    if (t0 + 2 < n_kv) tile(std::integral_constant<int, 2>{}, t0 + 2);
-    if constexpr (STAGES > 3) {
-      if (t0 + 3 < n_kv) tile(std::integral_constant<int, 3 % STAGES>{}, t0 + 3);
-    }
-    static_assert(STAGES <= 4, "unrolled for up to 4 stages");
+  // every wave's first masked chunk is at or after F
+  const int F = CAUSAL ? min(q0, N) / 32 : N / 32;
+  const int t_steady = min(n_kv - 1, F >= 1 ? (F - 1) / 2 : 0);
+  int t = 0;
+  for (; t < t_steady; ++t) {
+    const lds_u8* kt = stage_base(t);
+    chunk_step(kt, 0, kt, 1, 2 * t, std::false_type{});
+    publish_next(t);
+    chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::false_type{});
+  }
+  for (; t < n_kv; ++t) {
+    const lds_u8* kt = stage_base(t);
+    if (2 * t < n_ch) chunk_step(kt, 0, kt, 1, 2 * t, std::true_type{});
+    if (t + 1 < n_kv) publish_next(t);
+    if (2 * t + 1 < n_ch) chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::true_type{});
   }
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
