@@ -382,13 +382,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 //   dQ^T += K^T dS^T          (A: transposing reads of the K tile, B: dS^T packed)
 // dQ = scale * dQ^T at the end. K/V tiles of 64 keys stream through a ring of
 // STAGES stages with asynchronous direct copies, one barrier per tile.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int STAGES = 3>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int QPW = 32, NW = 8, BM = QPW * NW, BN = 64, STAGES = 3;
+  constexpr int QPW = 32, NW = 8, BM = QPW * NW, BN = 64;
   constexpr int QB = QPW / 16, DC = D / 32, DB = D / 16;
   constexpr int RB = 2 * D;  // bytes per tile row
-  constexpr int DO_BYTES = QB * DC * 64 * 16;  // one wave's dO^T fragments
   constexpr int TILE_BYTES = BN * RB;
   constexpr int COPIES_PER_WAVE = TILE_BYTES / 1024 / NW;
   constexpr int OPS = 2 * COPIES_PER_WAVE;  // copy instructions per wave per tile (K and V)
@@ -397,17 +396,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
   using Swz = DualSwizzle<D>;
   static_assert(COPIES_PER_WAVE >= 1 && TILE_BYTES % (1024 * NW) == 0, "K/V copy must split evenly over the waves");
 
-  // K/V ring, then each wave's dO^T fragments (kept in LDS rather than in
-  // registers: with two waves per SIMD the register file holds Q^T, the dQ^T
-  // accumulator and one chunk's working set, but not dO^T as well)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES + NW * DO_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int N = p.N;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, L = lane & 15;
-  lds_u8* const dot = smem + STAGES * 2 * TILE_BYTES + wave * DO_BYTES + lane * 16;
 
   const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
   const int b = tc.head / p.Hq;
@@ -440,9 +435,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
   };
   for (int t = 0; t < STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
 
-  // Q^T fragments (B operand) in registers, dO^T fragments in this wave's LDS
-  // region (lane-major, conflict free), the row's lse (log2 units) and D
-  bf16x8 qf[QB][DC];
+  // Q^T and dO^T fragments (B operands), the row's lse (log2 units) and D
+  bf16x8 qf[QB][DC], df[QB][DC];
   float lse2[QB], dl[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -452,7 +446,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qf[qb][dc] = __builtin_bit_cast(bf16x8, qs[dc * 4]);
-      *(FA_LDS u32x4*)(dot + (qb * DC + dc) * 1024) = ds[dc * 4];
+      df[qb][dc] = __builtin_bit_cast(bf16x8, ds[dc * 4]);
     }
     lse2[qb] = p.lse[qh + row] * 1.4426950408889634f;
     dl[qb] = p.delta[qh + row];
@@ -491,13 +485,11 @@ void fa_bwd_dq_kernel(BwdParams p) {
     for (int hb = 0; hb < 2; ++hb) {
       f32x4 s[QB], dp[QB];
       {
-        bf16x8 kf[DC], vf[DC], df[QB][DC];
+        bf16x8 kf[DC], vf[DC];
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
           kf[dc] = lds_read_b128(kt + hb * 16 * RB + r_off[dc]);
           vf[dc] = lds_read_b128(vt + hb * 16 * RB + r_off[dc]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) df[qb][dc] = lds_read_b128(dot + (qb * DC + dc) * 1024);
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
