@@ -134,7 +134,7 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
     kernels = {}
-    for key in ("fa_fwd_bf16_kernel", "fa_bwd_pre_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"):
+    for key in ("fa_fwd_bf16_kernel", "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"):
         fk = [n for n in fetch if key in n]
         wk = [n for n in write if key in n]
         if not fk or not wk:
@@ -233,7 +233,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     K = args.steps
     ev_f = [(hip.event(), hip.event()) for _ in range(K)]
-    ev_b = [(ctypes.c_void_p * 4)(*[hip.event() for _ in range(4)]) for _ in range(K)]
+    ev_b = [(ctypes.c_void_p * 3)(*[hip.event() for _ in range(3)]) for _ in range(K)]
     ev_all = (hip.event(), hip.event())
 
     def step(i=None):
@@ -267,9 +267,8 @@ def main():
     ms_step = total_ms / K
     kern_ms = {
         "fa_fwd_bf16_kernel": sum(hip.ms(a, b) for a, b in ev_f) / K,
-        "fa_bwd_pre_kernel": sum(hip.ms(e[0], e[1]) for e in ev_b) / K,
+        "fa_bwd_dq_kernel": sum(hip.ms(e[0], e[1]) for e in ev_b) / K,
         "fa_bwd_dkdv_kernel": sum(hip.ms(e[1], e[2]) for e in ev_b) / K,
-        "fa_bwd_dq_kernel": sum(hip.ms(e[2], e[3]) for e in ev_b) / K,
     }
     f_fwd, f_bwd = flops(B, H, N, d, causal)
     elt = 2
@@ -280,8 +279,6 @@ def main():
     # recomputes S and dP for it (executed, not counted as algorithmic work).
     work = {
         "fa_fwd_bf16_kernel": ("mfma", f_fwd),
-        # reads o, dO; writes D (fp32)
-        "fa_bwd_pre_kernel": ("hbm", 2 * qkv_bytes + 4 * B * H * N),
         "fa_bwd_dkdv_kernel": ("mfma", f_bwd * 4 / 5),
         "fa_bwd_dq_kernel": ("mfma", f_bwd * 1 / 5),
     }
@@ -308,7 +305,7 @@ def main():
             kernels[name] = {"avg_us": ms * 1e3, "gbs": u_ / (ms * 1e-3) / 1e9,
                              "frac_of_peak": u_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    bwd_ms = kern_ms["fa_bwd_pre_kernel"] + kern_ms["fa_bwd_dkdv_kernel"] + kern_ms["fa_bwd_dq_kernel"]
+    bwd_ms = kern_ms["fa_bwd_dkdv_kernel"] + kern_ms["fa_bwd_dq_kernel"]
     result = {
         "metric": "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak, d=128 N=4096",
         "value": value,

@@ -90,11 +90,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            hipStream_t stream);
 
 /* Instrumentation variant of fa_bwd for measurement: identical arguments and
- * results, plus `events`, an array of 4 hipEvent_t created by the caller (or
+ * results, plus `events`, an array of 3 hipEvent_t created by the caller (or
  * NULL, then this is exactly fa_bwd). The events are recorded on `stream`
- * before the row-term kernel, between it and the dK/dV kernel, between the
- * dK/dV kernel and the dQ kernel, and after the dQ kernel, so that each of
- * the three kernels can be timed on its own. */
+ * before the dQ kernel (which also computes the row term D), between it and
+ * the dK/dV kernel, and after the dK/dV kernel, so that each of the two
+ * kernels can be timed on its own. */
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,

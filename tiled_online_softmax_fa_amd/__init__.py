@@ -163,8 +163,8 @@ def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None, events=None):
     """Backward attention on bf16 tensors. Returns (dq, dk, dv).
 
-    events: optional ctypes array of 4 hipEvent_t handles; when given the call
-    goes through fa_bwd_timed, which records them around its three kernels.
+    events: optional ctypes array of 3 hipEvent_t handles; when given the call
+    goes through fa_bwd_timed, which records them around its two kernels.
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):

@@ -120,7 +120,7 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   if (st != FA_OK) return st;
   if (workspace_bytes < bwd_workspace(B, Hq, N, d)) return FA_ERR_INVALID_ARG;
   if (events != nullptr) {
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
       if (events[i] == nullptr) return FA_ERR_INVALID_ARG;
   }
   st = check_device();

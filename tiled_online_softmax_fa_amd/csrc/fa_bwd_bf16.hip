@@ -10,51 +10,29 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 // Grouped heads: the dK and dV of a key/value head sum over its query heads.
 //
-// Three kernels on the caller's stream:
-//   1. row term D (fp32);
+// Two kernels on the caller's stream, in this order:
+//   1. dQ: one workgroup per (query tile, batch * query head), built like the
+//      forward kernel: Q and dO stay in registers and K, V tiles stream
+//      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
+//      accumulates dQ^T += K^T dS^T. Its prologue also forms the row term D
+//      of its rows (fp32) and writes it for kernel 2. Recomputing S and dP
+//      here costs two more matrix products per tile than accumulating dQ
+//      inside kernel 2, but kernel 2 would have to add every key tile's
+//      contribution to dQ in memory (the atomics of "Flash Attention V3技术
+//      解析" section 2.1); the separate pass needs no atomics, no fp32
+//      accumulator, and gives a bitwise repeatable dQ;
 //   2. dK, dV: one workgroup per (key tile of 128 keys, batch * key/value
 //      head); query tiles of 64 rows (Q, dO, lse, D) stream through LDS (the
 //      tiled backward of the page "Flash Attention-2" (deepschool.ru),
 //      "Улучшение backward pass", and blogweb.cn section 5). Two waves per
 //      32-key slice split the work: one computes P and dV, the other dP, dS
-//      and dK (details at the kernel);
-//   3. dQ: one workgroup per (query tile, batch * query head), built like
-//      the forward kernel: Q and dO stay in registers and K, V tiles stream
-//      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
-//      accumulates dQ^T += K^T dS^T. Recomputing S and dP here costs two
-//      more matrix products per tile than accumulating dQ inside kernel 2,
-//      but kernel 2 would have to add every key tile's contribution to dQ in
-//      memory (the atomics of "Flash Attention V3技术解析" section 2.1); the
-//      separate pass needs no atomics, no fp32 accumulator, and gives a
-//      bitwise repeatable dQ.
+//      and dK (details at the kernel).
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 
-// ------------------------------------------------------------------ kernel 1: D
-// 16 lanes per row, 16 rows per workgroup of 256 threads.
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                         float* __restrict__ delta, long long rows) {
-  constexpr int PER_LANE = D / 16;  // 8 (d=128) or 4 (d=64) elements
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float s = 0.f;
-  if (row < rows) {
-    const __bf16* po = o + row * D + sub * PER_LANE;
-    const __bf16* pd = dout + row * D + sub * PER_LANE;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) s = fmaf((float)po[i], (float)pd[i], s);
-  }
-  s += __shfl_xor(s, 8, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 1, 16);
-  if (row < rows && sub == 0) delta[row] = s;
-}
-
-// ------------------------------------------------------------------ LDS layout shared by kernels 2 and 3
+// ------------------------------------------------------------------ LDS layout shared by both kernels
 //
 // Tiles here are read both row-wise (16-byte reads of one row's chunk) and
 // transposed (ds_read_b64_tr_b16), so the 16-byte chunk c of row r is stored
@@ -372,7 +350,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ kernel 3: dQ
+// ------------------------------------------------------------------ kernel 1: dQ (and D)
 //
 // One workgroup of 8 waves per (query tile of 256 rows, batch * query head);
 // each wave owns 32 query rows. Per 32-key chunk, with keys on the
@@ -443,13 +421,19 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int row = min(qw0 + qb * 16 + L, N - 1);
     const u32x4* qs = (const u32x4*)((const __bf16*)p.q + (qh + row) * D + g * 8);
     const u32x4* ds = (const u32x4*)((const __bf16*)p.dout + (qh + row) * D + g * 8);
+    const u32x4* os = (const u32x4*)((const __bf16*)p.o + (qh + row) * D + g * 8);
+    float dsum = 0.f;  // this lane's part of D = sum_c dO_c O_c (d = 32 dc + 8 g + e)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qf[qb][dc] = __builtin_bit_cast(bf16x8, qs[dc * 4]);
       df[qb][dc] = __builtin_bit_cast(bf16x8, ds[dc * 4]);
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, os[dc * 4]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)df[qb][dc][e], (float)ov[e], dsum);
     }
     lse2[qb] = p.lse[qh + row] * 1.4426950408889634f;
-    dl[qb] = p.delta[qh + row];
+    dl[qb] = sum_over_row_groups(dsum);  // the four lanes of the row hold its four d-slices
+    if (g == 0 && qw0 + qb * 16 + L < N) p.delta[qh + row] = dl[qb];  // for the dK/dV kernel
   }
   f32x4 acc[DB][QB];
 #pragma unroll
@@ -592,11 +576,11 @@ void fa_bwd_dq_kernel(BwdParams p) {
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipEvent_t* ev) {
   BwdParams p = p_in;
-  const long long rows = (long long)p.B * p.Hq * p.N;
   hipError_t e;
+  // dQ first: it also writes the row term D that the dK/dV kernel reads
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     (const __bf16*)p.o, (const __bf16*)p.dout, p.delta, rows);
+  p.n_tiles = (p.N + 255) / 256;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + 127) / 128;
@@ -604,10 +588,6 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  p.n_tiles = (p.N + 255) / 256;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -386,7 +386,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 // ------------------------------------------------------------------ launch
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream) {
-  constexpr int QPW = 32, NW = 8, STAGES = 4;
+  constexpr int QPW = 32, NW = 8, STAGES = 3;
   FwdParams p = p_in;
   p.n_tiles = (p.N + QPW * NW - 1) / (QPW * NW);
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
