@@ -89,6 +89,58 @@ def measured_traffic(kernel_key, launches_note):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+
+
+def time_configs(torch, min_warmup_s):
+    """Forward time of each forward workload (seeded inputs resident on the GPU, HIP events on the launch stream)."""
+    import numpy as np
+
+    import tiled_online_softmax_fa_amd as fa
+    from fa_inputs import WORKLOADS, make_workload_inputs
+
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    for w in WORKLOADS.values():
+        if w.backward:
+            continue
+        inp = make_workload_inputs(w)
+        if w.dtype == "bf16":
+            dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+                   for n in ("q", "k", "v")}
+            call, elt, peak = fa.fwd, 2, PEAK_BF16_TFLOPS
+        else:
+            dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to("cuda:0")
+                   for n in ("q", "k", "v")}
+            call, elt, peak = fa.fwd_f32, 4, PEAK_F32_TFLOPS
+        o, lse = call(dev["q"], dev["k"], dev["v"], causal=w.causal)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 20 or time.perf_counter() - t0 < min_warmup_s:
+            call(dev["q"], dev["k"], dev["v"], causal=w.causal, out=o, lse=lse)
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        K = 50
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(K):
+            call(dev["q"], dev["k"], dev["v"], causal=w.causal, out=o, lse=lse)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us = hip.ms(e0, e1) / K * 1e3
+        f_fwd, _ = flops(w.B, w.Hq, w.N, w.d, w.causal)
+        nbytes = (2 * w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d * elt + 4 * w.B * w.Hq * w.N
+        tflops = f_fwd / (us * 1e-6) / 1e12
+        print(json.dumps({"workload": w.name, "dtype": w.dtype, "causal": w.causal,
+                          "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "avg_us": us,
+                          "tflops": tflops, "frac_of_peak": tflops / peak, "peak_tflops": peak,
+                          "compulsory_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+                          "source_digest": source_digest()}), flush=True)
+    return 0
+
+
 COPY_BYTES = 1 << 29  # 512 MiB read and 512 MiB written per calibration copy
 COPY_LAUNCHES = 4
 
@@ -197,6 +249,9 @@ def main():
                     help="keep warming up until this many seconds have passed (0 for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM byte counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="only time the forward on every forward workload of fa_inputs.WORKLOADS "
+                         "(one JSON line each; not the headline line)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs "
                          "of a short bench run and of a --copy-calibration run (no GPU needed)")
@@ -213,6 +268,8 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration(torch)
+    if args.configs:
+        return time_configs(torch, args.min_warmup_s)
 
     import tiled_online_softmax_fa_amd as fa
     from fa_inputs import make_inputs

@@ -8,8 +8,9 @@
 // This path serves short, latency-bound problems (its measured case is one
 // head of 256 keys), so it favours simplicity: 4 waves x 16 query rows per
 // workgroup (the 64-row query block of the mhpq.cn page, section 3.1),
-// 32-key K/V tiles staged through LDS with a single buffer, and rows padded to
-// d + 4 floats so the fragment reads of 16 consecutive rows fall in different
+// 32-key K/V tiles staged through two LDS buffers (each tile's global loads
+// are issued one tile ahead, into registers), and rows padded to d + 4
+// floats so the fragment reads of 16 consecutive rows fall in different
 // banks (the row padding of mhpq.cn section 5.2).
 //
 // The P^T accumulator registers feed O^T += V^T P^T directly: for the r-th
@@ -29,8 +30,9 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
   constexpr int DS = D / 4;   // k-steps of S^T
   constexpr int DB = D / 16;  // 16-row blocks of O^T
   constexpr int LD = D + 4;   // padded LDS row (floats)
-  __shared__ __attribute__((aligned(16))) float ks[BN * LD];
-  __shared__ __attribute__((aligned(16))) float vs[BN * LD];
+  // two K/V tile buffers: tile t+1 is written while tile t is read
+  __shared__ __attribute__((aligned(16))) float ks2[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) float vs2[2][BN * LD];
 
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -66,19 +68,37 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
   float m_ref = kNegInf, l_part = 0.f;
   const float c = p.scale_log2;
 
+  // Tile loads go global -> registers one tile ahead (their latency overlaps
+  // the math of the current tile), then registers -> LDS at the top of the
+  // next iteration; one barrier per tile publishes the tile and, with two
+  // buffers, also guarantees the buffer written next is no longer read.
+  constexpr int VEC = BN * D / 4;             // float4 pieces per tensor
+  constexpr int PER = VEC / (NW * 64);        // pieces per thread
+  static_assert(VEC % (NW * 64) == 0, "tile split");
+  f32x4 kreg[PER], vreg[PER];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * NW * 64;
+      const int row = i / (D / 4), c4 = i % (D / 4);
+      const int grow = min(t * BN + row, N - 1);
+      kreg[j] = *(const f32x4*)(kg + (size_t)grow * D + c4 * 4);
+      vreg[j] = *(const f32x4*)(vg + (size_t)grow * D + c4 * 4);
+    }
+  };
+  if (n_kv > 0) load_tile(0);
   for (int t = 0; t < n_kv; ++t) {
     const int kv0 = t * BN;
-    __syncthreads();  // previous tile fully consumed
-    constexpr int VEC = BN * D / 4;  // float4 pieces per tensor
+    float* ks = ks2[t & 1];
+    float* vs = vs2[t & 1];
 #pragma unroll
-    for (int i = tid; i < VEC; i += NW * 64) {
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * NW * 64;
       const int row = i / (D / 4), c4 = i % (D / 4);
-      const int grow = min(kv0 + row, N - 1);
-      const f32x4 kv = *(const f32x4*)(kg + (size_t)grow * D + c4 * 4);
-      const f32x4 vv = *(const f32x4*)(vg + (size_t)grow * D + c4 * 4);
-      *(f32x4*)(ks + row * LD + c4 * 4) = kv;
-      *(f32x4*)(vs + row * LD + c4 * 4) = vv;
+      *(f32x4*)(ks + row * LD + c4 * 4) = kreg[j];
+      *(f32x4*)(vs + row * LD + c4 * 4) = vreg[j];
     }
+    if (t + 1 < n_kv) load_tile(t + 1);
     __syncthreads();
     if (t >= n_kv_wave) continue;
 
