@@ -138,6 +138,44 @@ def time_configs(torch, min_warmup_s):
                           "tflops": tflops, "frac_of_peak": tflops / peak, "peak_tflops": peak,
                           "compulsory_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
                           "source_digest": source_digest()}), flush=True)
+
+    # split-KV on shapes with few query tiles (seeded N(0,1) inputs, bf16): plain forward vs key-range parts
+    from fa_inputs import Workload
+
+    for B, H, N, d, causal in ((1, 8, 16384, 128, True), (1, 4, 8192, 128, False)):
+        w = Workload(f"splitkv_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9)
+        inp = make_workload_inputs(w)
+        dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+               for n in ("q", "k", "v")}
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        f_fwd, _ = flops(B, H, N, d, causal)
+        for splits in (0, 2, 4, 8):
+            if splits:
+                ws = torch.empty(fa.splitkv_workspace_bytes(B, H, H, N, d, splits), dtype=torch.uint8, device="cuda:0")
+                run = lambda: fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], splits, causal=causal, out=o, lse=lse,
+                                             workspace=ws)
+            else:
+                run = lambda: fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, out=o, lse=lse)
+            t0 = time.perf_counter()
+            n = 0
+            while n < 10 or time.perf_counter() - t0 < min(min_warmup_s, 0.5):
+                run()
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(20):
+                run()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            us = hip.ms(e0, e1) / 20 * 1e3
+            tflops = f_fwd / (us * 1e-6) / 1e12
+            print(json.dumps({"workload": w.name, "entry": "fa_fwd_splitkv" if splits else "fa_fwd", "n_splits": splits,
+                              "avg_us": us, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+                              "source_digest": source_digest()}), flush=True)
     return 0
 
 

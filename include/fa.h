@@ -72,6 +72,28 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                hipStream_t stream);
 
+/* Bytes of device workspace fa_fwd_splitkv needs for these sizes and
+ * n_splits (0 on invalid sizes or n_splits outside 1..64). */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int n_splits);
+
+/* Forward attention, bf16, with the keys of every query tile split into
+ * n_splits contiguous ranges processed by separate workgroups: more
+ * parallelism when B * Hq * ceil(N / 256) workgroups cannot fill the GPU
+ * (few heads, long sequences). Each range produces its partial output
+ * O_s (fp32, normalised by its own row sum) and lse_s; a second kernel
+ * combines them with the online-softmax rule one level up, lse = log sum_s
+ * exp(lse_s), O = sum_s exp(lse_s - lse) O_s (the merge of per-device
+ * partial results in "FlashAttention技术解析" (mhpq.cn), section 4.2).
+ * Same arguments, layouts and results as fa_fwd (up to rounding), plus
+ * workspace: device memory of at least fa_fwd_splitkv_workspace_bytes(...)
+ * bytes, 16-byte aligned, contents ignored on entry.
+ * n_splits: 1..64 (FA_ERR_INVALID_ARG otherwise); ranges are balanced over
+ * the key tiles each query tile actually visits (causal included). */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   int n_splits, hipStream_t stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (0 on invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

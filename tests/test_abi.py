@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_f32",
-                                    "fa_status_string"]
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -90,6 +90,32 @@ def test_backward_argument_errors():
     assert call(ptrs=[BAD] * 9 + [NULL]) == INV
     assert call(scale=-1.0) == INV
     assert call(B=0, ptrs=[NULL] * 10, wsb=0) == FA_OK
+
+
+def test_splitkv_argument_errors():
+    from tiled_online_softmax_fa_amd import FA_ERR_INVALID_ARG as INV, FA_ERR_UNSUPPORTED as UNS, FA_OK
+
+    lib = _lib()
+    ws = lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 3)
+    assert ws >= 3 * (2 * 8 * 64 * 4 + 2 * 8 * 4)
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 0) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 65) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 96, 2) == 0
+
+    def call(ptrs=None, wsb=ws, splits=3, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125)
+        a.update(kw)
+        p = ptrs or [BAD] * 6
+        return lib.fa_fwd_splitkv(*p, wsb, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"],
+                                  splits, NULL)
+
+    assert call(d=96) == UNS
+    assert call(splits=0) == INV
+    assert call(splits=65) == INV
+    assert call(wsb=ws - 1) == INV
+    assert call(ptrs=[BAD] * 5 + [NULL]) == INV
+    assert call(Hq=3, Hkv=2) == INV
+    assert call(B=0, ptrs=[NULL] * 6, wsb=0) == FA_OK
 
 
 def test_status_strings():

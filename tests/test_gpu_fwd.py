@@ -4,7 +4,7 @@ import sys
 import numpy as np
 import pytest
 
-from fa_inputs import WORKLOADS, make_workload_inputs
+from fa_inputs import WORKLOADS, make_inputs, make_workload_inputs
 from fa_testlib import (F32_MAX_ABS, LSE_MAX_ABS, assert_bf16_close, errors, run_fwd, to_device, to_f64,
                         torch_mod)
 from oracle import attention_fwd, attention_fwd_rows
@@ -163,6 +163,61 @@ def test_fwd_bf16_workload_causal_gqa_4096():
     w = WORKLOADS["fwd_causal_gqa_bf16_b2hq64hkv8n4096d128"]
     _say(f"workload {w.name} (sampled rows + full heads)")
     _sampled_check(w, rows_per_head=16)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,causal", [(4, 2, 128, True), (2, 2, 64, False)])
+def test_fwd_bf16_long_sequence_16384(Hq, Hkv, d, causal):
+    # 64 (causal: 1 to 256) key tiles per query tile: sampled rows against the oracle
+    from fa_inputs import Workload
+
+    w = Workload(f"long_b1hq{Hq}hkv{Hkv}n16384d{d}", 1, Hq, Hkv, 16384, d, "bf16", causal, seed=77)
+    _say(f"workload {w.name} (sampled rows)")
+    _sampled_check(w, n_full_heads=0, rows_per_head=24)
+
+
+SPLITKV = [
+    # B, Hq, Hkv, N, d, causal, n_splits  -- including more parts than key tiles (empty parts)
+    (1, 2, 2, 300, 64, False, 2),
+    (1, 2, 2, 300, 128, True, 3),
+    (2, 8, 2, 513, 128, True, 4),
+    (1, 4, 1, 1000, 64, True, 7),
+    (1, 1, 1, 2048, 128, True, 16),
+    (1, 2, 2, 2048, 64, False, 5),
+    (1, 2, 2, 17, 128, True, 5),
+    (1, 1, 1, 1, 64, False, 2),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,n_splits", SPLITKV)
+def test_fwd_splitkv_small(B, Hq, Hkv, N, d, causal, n_splits):
+    import tiled_online_softmax_fa_amd as fa
+
+    inp = make_inputs(B, Hq, Hkv, N, d, "bf16", seed=N + 13 * n_splits)
+    scale = d ** -0.5
+    o, lse = fa.fwd_splitkv(*(to_device(inp, n, "bf16") for n in ("q", "k", "v")), n_splits, causal=causal,
+                            scale=scale)
+    torch_mod().cuda.synchronize()
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    mx, mean = assert_bf16_close(to_f64(o), O, f"split-KV x{n_splits} O")
+    assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
+    _say(f"  split-KV x{n_splits}: O max {mx:.2e} mean {mean:.2e}")
+
+
+def test_fwd_splitkv_long_sequence_16384():
+    from fa_inputs import Workload
+    import tiled_online_softmax_fa_amd as fa
+
+    w = Workload("long_split_b1hq4hkv2n16384d128", 1, 4, 2, 16384, 128, "bf16", True, seed=78)
+    inp = make_workload_inputs(w)
+    o, lse = fa.fwd_splitkv(*(to_device(inp, n, "bf16") for n in ("q", "k", "v")), 8, causal=True, scale=w.scale)
+    torch_mod().cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    rng = np.random.default_rng(5)
+    for h in range(w.Hq):
+        rows = np.unique(np.concatenate([[0, 1, 255, 256, w.N - 1], rng.integers(0, w.N, 24)]))
+        Or, Lr = attention_fwd_rows(inp["q"], inp["k"], inp["v"], True, w.scale, 0, h, rows)
+        assert errors(o[0, h, rows], Or)[0] <= 2e-2
+        assert errors(lse[0, h, rows], Lr)[0] <= LSE_MAX_ABS
 
 
 def test_fwd_bf16_is_bitwise_repeatable():

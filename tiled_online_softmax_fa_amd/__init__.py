@@ -23,6 +23,8 @@ __all__ = [
     "load_library",
     "fwd",
     "fwd_f32",
+    "fwd_splitkv",
+    "splitkv_workspace_bytes",
     "bwd",
     "bwd_workspace_bytes",
     "flash_attn",
@@ -71,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp, vp]
     lib.fa_bwd_timed.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -154,6 +160,37 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
 def fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
     """Forward attention on float32 tensors. Returns (o, lse)."""
     return _fwd_impl("fa_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse)
+
+
+def splitkv_workspace_bytes(B, Hq, Hkv, N, d, n_splits) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, n_splits))
+
+
+def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, out=None, lse=None, workspace=None):
+    """Forward attention on bf16 tensors with each query tile's keys split into n_splits ranges
+    (separate workgroups, then a merge). Same results as fwd up to rounding. Returns (o, lse)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require(out, torch.bfloat16, "out")
+    _require(lse, torch.float32, "lse")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    need = splitkv_workspace_bytes(B, Hq, Hkv, N, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), int(n_splits), _stream_ptr(q))
+    _check(st, "fa_fwd_splitkv")
+    return out, lse
 
 
 def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:

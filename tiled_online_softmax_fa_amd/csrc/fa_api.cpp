@@ -85,6 +85,18 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
                             : fa::launch_fwd_f32(p, d, causal != 0, stream));
 }
 
+constexpr int kMaxSplits = 64;
+
+// split-KV workspace: o_part [S][rows][d] fp32, then (256-byte aligned) lse_part [S][rows] fp32
+size_t splitkv_o_bytes(int B, int Hq, int N, int d, int n_splits) {
+  const size_t rows = (size_t)B * Hq * N;
+  return (rows * (size_t)d * sizeof(float) * (size_t)n_splits + 255) & ~(size_t)255;
+}
+size_t splitkv_workspace(int B, int Hq, int N, int d, int n_splits) {
+  const size_t rows = (size_t)B * Hq * N;
+  return splitkv_o_bytes(B, Hq, N, d, n_splits) + ((rows * sizeof(float) * (size_t)n_splits + 255) & ~(size_t)255);
+}
+
 size_t bwd_workspace(int B, int Hq, int N, int d) {
   const size_t rows = (size_t)B * Hq * N;
   (void)d;
@@ -103,6 +115,41 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int N,
                int d, int causal, float scale, hipStream_t stream) {
   return fwd_common<float>(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, false);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int n_splits) {
+  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f) != FA_OK) return 0;
+  if (n_splits < 1 || n_splits > kMaxSplits) return 0;
+  return splitkv_workspace(B, Hq, N, d, n_splits);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale, int n_splits,
+                   hipStream_t stream) {
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q, k, v, o, lse, workspace});
+  if (st != FA_OK) return st;
+  if (workspace_bytes < splitkv_workspace(B, Hq, N, d, n_splits)) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.scale_log2 = scale * kLog2e;
+  p.n_splits = n_splits;
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)((char*)workspace + splitkv_o_bytes(B, Hq, N, d, n_splits));
+  return launch_status(fa::launch_fwd_bf16_splitkv(p, d, causal != 0, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {

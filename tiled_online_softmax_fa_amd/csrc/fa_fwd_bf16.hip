@@ -83,7 +83,10 @@ struct KVSwizzle {
 // wave's issue priority around its runs of matrix instructions, so the wave
 // that has MFMA work ready wins the issue slot and the other wave's vector
 // work fills the gaps.
-template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES>
+// SPLIT: the workgroup processes part blockIdx.x / (n_tiles * B * Hq) of the
+// query tile's key tiles and writes that part's O (fp32) and lse to
+// p.o_part / p.lse_part for the merge kernel, instead of O and lse.
+template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
 void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = QPW * NW, BN = 64;
@@ -111,7 +114,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int g = lane >> 4;   // row group of an accumulator block
   const int L = lane & 15;   // column of an accumulator block (this lane's query)
 
-  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
+  const int n_wg = p.n_tiles * p.B * p.Hq;  // workgroups per part
+  const int part = SPLIT ? (int)blockIdx.x / n_wg : 0;
+  const TileCoord tc = map_workgroup(SPLIT ? (int)blockIdx.x - part * n_wg : (int)blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
   const int b = tc.head / p.Hq;
   const int h = tc.head - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);
@@ -124,15 +129,20 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int q0 = tc.tile * BM;
   const int qw0 = q0 + wave * QPW;  // first query row of this wave
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_kv = (kv_end + BN - 1) / BN;  // tiles loaded by the workgroup
-  // chunks this wave processes, and the first one that needs an element mask
-  const int n_ch = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
-  const int first_mask = min(n_ch, CAUSAL ? min((qw0 + 1) / 32, N / 32) : N / 32);
+  const int n_kv_all = (kv_end + BN - 1) / BN;  // key tiles with a visible key for the workgroup
+  // this workgroup's key tiles [t_lo, n_kv) (all of them without SPLIT)
+  const int t_lo = SPLIT ? (int)(((long long)part * n_kv_all) / p.n_splits) : 0;
+  const int n_kv = SPLIT ? (int)(((long long)(part + 1) * n_kv_all) / p.n_splits) : n_kv_all;
+  // chunks this wave processes [c_lo, n_ch), and the first one that needs an element mask
+  const int n_ch_all = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
+  const int n_ch = min(n_ch_all, 2 * n_kv);
+  const int c_lo = 2 * t_lo;
+  const int first_mask = min(n_ch_all, CAUSAL ? min((qw0 + 1) / 32, N / 32) : N / 32);
 
   // ---- K/V tile copies (asynchronous; published by the barrier of the tile)
   auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t * BN;
-    const uint32_t kdst = lds_address(smem) + (t % STAGES) * 2 * TILE_BYTES;
+    const uint32_t kdst = lds_address(smem) + ((t - t_lo) % STAGES) * 2 * TILE_BYTES;
 #pragma unroll
     for (int c = 0; c < COPIES_PER_WAVE; ++c) {
       const int piece = wave * COPIES_PER_WAVE + c;
@@ -146,7 +156,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  for (int t = 0; t < STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
+  for (int t = t_lo; t < t_lo + STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
 
   // Q^T fragments (B operand of S^T = K Q^T), held for the whole key loop.
   bf16x8 qf[QB][DC];
@@ -322,7 +332,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // run in a loop of their own with branch-free bodies; the diagonal and the
   // end of the sequence take the masked path. Stage bases are run-time values.
   auto stage_base = [&](int t) __attribute__((always_inline)) {
-    return smem + uniform((t % STAGES) * 2 * TILE_BYTES);
+    return smem + uniform(((t - t_lo) % STAGES) * 2 * TILE_BYTES);
   };
   auto publish_next = [&](int t) __attribute__((always_inline)) {
     if (t + STAGES - 2 < n_kv) {
@@ -333,25 +343,25 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
   };
-  if (n_kv > 0) {
-    if (n_kv >= STAGES - 1) {
+  if (n_kv > t_lo) {
+    if (n_kv - t_lo >= STAGES - 1) {
       wait_vmcnt_le<(STAGES - 2) * OPS>();  // tile 0 landed; tiles 1..STAGES-2 may still fly
     } else {
       wait_vmcnt0();
     }
     __syncthreads();
-    if (n_ch > 0) {
-      if (first_mask > 0) {
-        scores(smem, 0, 0, std::false_type{});
+    if (n_ch > c_lo) {
+      if (first_mask > c_lo) {
+        scores(smem, 0, c_lo, std::false_type{});
       } else {
-        scores(smem, 0, 0, std::true_type{});
+        scores(smem, 0, c_lo, std::true_type{});
       }
     }
   }
   // every wave's first masked chunk is at or after F
   const int F = CAUSAL ? min(q0, N) / 32 : N / 32;
   const int t_steady = min(n_kv - 1, F >= 1 ? (F - 1) / 2 : 0);
-  int t = 0;
+  int t = t_lo;
   for (; t < t_steady; ++t) {
     const lds_u8* kt = stage_base(t);
     chunk_step(kt, 0, kt, 1, 2 * t, std::false_type{});
@@ -371,16 +381,56 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const float l = sum_over_row_groups(l_part[qb]);
     const int row = qw0 + qb * 16 + L;
     if (row < N) {
-      const float inv = 1.0f / l;
+      if constexpr (SPLIT) {
+        // this part's O (fp32) and lse; a row with no key in the part (l = 0)
+        // gets O = 0, lse = -inf, which the merge weighs by exp(-inf) = 0
+        const size_t prow = ((size_t)part * p.B * p.Hq + (size_t)(b * p.Hq + h)) * N + row;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 o4 = acc[db][qb] * inv;
-        u32x2 packed = {pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
-        *(u32x2*)(og + (size_t)row * D + db * 16 + g * 4) = packed;
+        for (int db = 0; db < DB; ++db) *(f32x4*)(p.o_part + prow * D + db * 16 + g * 4) = acc[db][qb] * inv;
+        if (g == 0) p.lse_part[prow] = l > 0.f ? (m_ref[qb] + log2_fast(l)) * kLn2 : kNegInf;
+      } else {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const f32x4 o4 = acc[db][qb] * inv;
+          u32x2 packed = {pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
+          *(u32x2*)(og + (size_t)row * D + db * 16 + g * 4) = packed;
+        }
+        if (g == 0) lseg[row] = (m_ref[qb] + log2_fast(l)) * kLn2;
       }
-      if (g == 0) lseg[row] = (m_ref[qb] + log2_fast(l)) * kLn2;
     }
   }
+}
+
+// ------------------------------------------------------------------ split-KV merge
+//
+// The partial results of the key-range parts of a row are combined with the
+// online-softmax rule one level up (the merge of per-device partial results
+// in "FlashAttention技术解析" section 4.2): lse = log sum_s exp(lse_s),
+// O = sum_s exp(lse_s - lse) O_s. D / 4 lanes per row, 4 columns each.
+template <int D>
+__global__ __launch_bounds__(256) void fa_fwd_merge_kernel(FwdParams p, long long rows) {
+  constexpr int LPR = D / 4;  // lanes per row
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c4 = threadIdx.x % LPR;
+  if (row >= rows) return;
+  const int S = p.n_splits;
+  float m = kNegInf;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, p.lse_part[(size_t)s * rows + row]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != kNegInf) {  // always true for a valid row (key 0 is visible to every query)
+    for (int s = 0; s < S; ++s) {
+      const float w = __expf(p.lse_part[(size_t)s * rows + row] - m);
+      wsum += w;
+      o += w * *(const f32x4*)(p.o_part + ((size_t)s * rows + row) * D + c4 * 4);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  o *= inv;
+  *(u32x2*)((__bf16*)p.o + row * D + c4 * 4) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  if (c4 == 0) p.lse[row] = m + __logf(wsum);
 }
 
 // ------------------------------------------------------------------ launch
@@ -392,6 +442,28 @@ static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream)
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, QPW, NW, true, STAGES>), dim3(grid), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_split_cfg(const FwdParams& p_in, hipStream_t stream) {
+  constexpr int QPW = 32, NW = 8, STAGES = 3;
+  FwdParams p = p_in;
+  p.n_tiles = (p.N + QPW * NW - 1) / (QPW * NW);
+  const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq * p.n_splits);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, QPW, NW, true, STAGES, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)p.B * p.Hq * p.N;
+  const long long rows_per_block = 256 / (D / 4);
+  hipLaunchKernelGGL((fa_fwd_merge_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256), 0,
+                     stream, p, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_fwd_bf16_split_cfg<128, true>(p, stream) : launch_fwd_bf16_split_cfg<128, false>(p, stream);
+  if (d == 64) return causal ? launch_fwd_bf16_split_cfg<64, true>(p, stream) : launch_fwd_bf16_split_cfg<64, false>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {

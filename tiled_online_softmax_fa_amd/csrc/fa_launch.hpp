@@ -15,6 +15,12 @@ struct FwdParams {
   int B, Hq, Hkv, N;
   float scale_log2;  // scale * log2(e): scores are exponentiated with exp2
   int n_tiles;       // query tiles per head (filled in by the launcher)
+  // split-KV only: key-range parts per query tile, and the per-part outputs
+  // o_part [n_splits][B*Hq][N][d] fp32 (normalised by the part's own row sum)
+  // and lse_part [n_splits][B*Hq][N] fp32 (natural log; -inf for no key)
+  int n_splits;
+  float* o_part;
+  float* lse_part;
 };
 
 struct BwdParams {
@@ -36,7 +42,9 @@ struct BwdParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
-// events: NULL or 4 events recorded before/between/after the three backward kernels
+// split-KV forward: the partial kernel then the merge (p.n_splits >= 1, workspace in p.o_part / p.lse_part)
+hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// events: NULL or 3 events recorded before/between/after the two backward kernels
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* events);
 
 }  // namespace fa
