@@ -139,18 +139,22 @@ def time_configs(torch, min_warmup_s):
                           "compulsory_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
                           "source_digest": source_digest()}), flush=True)
 
-    # split-KV on shapes with few query tiles (seeded N(0,1) inputs, bf16): plain forward vs key-range parts
+    # head dim 256, and split-KV on shapes with few query tiles (seeded N(0,1) inputs, bf16): plain forward
+    # vs key-range parts
     from fa_inputs import Workload
 
-    for B, H, N, d, causal in ((1, 8, 16384, 128, True), (1, 4, 8192, 128, False)):
-        w = Workload(f"splitkv_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9)
+    for B, H, N, d, causal, split_list in ((2, 16, 4096, 256, True, (0,)), (2, 16, 4096, 256, False, (0,)),
+                                          (1, 8, 16384, 128, True, (0, 2, 4, 8)),
+                                          (1, 4, 8192, 128, False, (0, 2, 4, 8))):
+        w = Workload(f"{'splitkv_' if len(split_list) > 1 else 'fwd_'}b{B}h{H}n{N}d{d}{'_causal' if causal else ''}",
+                     B, H, H, N, d, "bf16", causal, seed=9)
         inp = make_workload_inputs(w)
         dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
                for n in ("q", "k", "v")}
         o = torch.empty_like(dev["q"])
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
         f_fwd, _ = flops(B, H, N, d, causal)
-        for splits in (0, 2, 4, 8):
+        for splits in split_list:
             if splits:
                 ws = torch.empty(fa.splitkv_workspace_bytes(B, H, H, N, d, splits), dtype=torch.uint8, device="cuda:0")
                 run = lambda: fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], splits, causal=causal, out=o, lse=lse,

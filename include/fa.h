@@ -60,14 +60,15 @@ typedef enum {
 
 /* Forward, bf16 storage (q, k, v, o as bf16 bit patterns), float32 arithmetic
  * for the softmax and the accumulators, float32 lse. o is rounded to bf16
- * round-to-nearest-even. Supported d: 64, 128. Sizes: B >= 0, N >= 0,
+ * round-to-nearest-even. Supported d: 64, 128, 256. Sizes: B >= 0, N >= 0,
  * Hq >= 1, Hkv >= 1, Hq % Hkv == 0, B*Hq*N*d < 2^31 elements per tensor. */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
            hipStream_t stream);
 
 /* Forward, float32 storage and float32 arithmetic throughout (no bf16
- * rounding anywhere). Same arguments, layouts and limits as fa_fwd. */
+ * rounding anywhere). Same arguments, layouts and limits as fa_fwd, except
+ * that d is 64 or 128. */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                hipStream_t stream);

@@ -50,7 +50,9 @@ def test_forward_argument_errors(entry):
 
     lib = _lib()
     assert _fwd(lib, d=96, entry=entry) == UNS
-    assert _fwd(lib, d=256, entry=entry) == UNS
+    assert _fwd(lib, d=512, entry=entry) == UNS
+    # head dim 256: bf16 forward only (there validation goes on to the pointer check)
+    assert _fwd(lib, d=256, ptrs=[NULL] * 5, entry=entry) == (INV if entry == "fa_fwd" else UNS)
     assert _fwd(lib, Hq=3, Hkv=2, entry=entry) == INV
     assert _fwd(lib, Hkv=0, entry=entry) == INV
     assert _fwd(lib, B=-1, entry=entry) == INV
@@ -85,6 +87,8 @@ def test_backward_argument_errors():
         return lib.fa_bwd(*p, wsb, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], NULL)
 
     assert call(d=80) == UNS
+    assert call(d=256) == UNS
+    assert lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 256) == 0
     assert call(Hq=4, Hkv=3) == INV
     assert call(wsb=ws - 1) == INV
     assert call(ptrs=[BAD] * 9 + [NULL]) == INV
@@ -110,6 +114,8 @@ def test_splitkv_argument_errors():
                                   splits, NULL)
 
     assert call(d=96) == UNS
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 256, 2) >= 2 * (2 * 8 * 256 * 4 + 2 * 8 * 4)
+    assert call(d=256, ptrs=[NULL] * 6) == INV
     assert call(splits=0) == INV
     assert call(splits=65) == INV
     assert call(wsb=ws - 1) == INV

@@ -33,6 +33,14 @@ SMALL = [
     (1, 2, 2, 17, 128, True),
     (1, 2, 2, 64, 64, True),
     (1, 1, 1, 2048, 128, True),
+    # head dim 256 (32-key tiles, 128-query tiles)
+    (1, 2, 2, 300, 256, False),
+    (1, 2, 2, 300, 256, True),
+    (2, 4, 2, 513, 256, True),
+    (1, 2, 1, 129, 256, False),
+    (1, 1, 1, 1, 256, True),
+    (1, 2, 2, 31, 256, True),
+    (1, 1, 1, 1024, 256, True),
 ]
 
 
@@ -48,7 +56,7 @@ def test_fwd_bf16_small(B, Hq, Hkv, N, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fwd_bf16_peaky_scores(causal, d):
     # q scaled by 8: softmax rows are dominated by a few keys and the running
     # maximum moves often, exercising the rescale path
@@ -165,7 +173,7 @@ def test_fwd_bf16_workload_causal_gqa_4096():
     _sampled_check(w, rows_per_head=16)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d,causal", [(4, 2, 128, True), (2, 2, 64, False)])
+@pytest.mark.parametrize("Hq,Hkv,d,causal", [(4, 2, 128, True), (2, 2, 64, False), (2, 1, 256, True)])
 def test_fwd_bf16_long_sequence_16384(Hq, Hkv, d, causal):
     # 64 (causal: 1 to 256) key tiles per query tile: sampled rows against the oracle
     from fa_inputs import Workload
@@ -185,6 +193,8 @@ SPLITKV = [
     (1, 2, 2, 2048, 64, False, 5),
     (1, 2, 2, 17, 128, True, 5),
     (1, 1, 1, 1, 64, False, 2),
+    (1, 2, 2, 300, 256, True, 3),
+    (1, 2, 1, 1000, 256, False, 4),
 ]
 
 
@@ -245,6 +255,10 @@ def test_fwd_empty_and_errors():
     q = torch.zeros((1, 2, 8, 96), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(fa.FaError) as e:
         fa.fwd(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    q = torch.zeros((1, 2, 8, 256), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd_f32(q, q, q)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     q = torch.zeros((1, 3, 8, 64), dtype=torch.bfloat16, device="cuda:0")
     k = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda:0")

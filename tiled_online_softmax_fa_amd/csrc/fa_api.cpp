@@ -19,12 +19,13 @@ std::atomic<int> g_arch_state[kMaxDevices];
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shapes common to forward and backward. Returns FA_OK, or the error code.
-int check_shapes(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+// Head dims: 64 and 128 everywhere, 256 where `d256` (the bf16 forward).
+int check_shapes(int B, int Hq, int Hkv, int N, int d, int causal, float scale, bool d256 = false) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && !(d256 && d == 256)) return FA_ERR_UNSUPPORTED;
   // every tensor must index with 32-bit element offsets inside one head and
   // with size_t across heads; keep the whole tensor below 2^31 elements
   const long long elems = (long long)B * Hq * N * d;
@@ -63,7 +64,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename T>
 int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int Hq, int Hkv, int N, int d,
                int causal, float scale, hipStream_t stream, bool bf16) {
-  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, bf16);
   if (st != FA_OK) return st;
   if (B == 0 || N == 0) return FA_OK;
   st = check_ptrs({q, k, v, o, lse});
@@ -118,7 +119,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int n_splits) {
-  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f) != FA_OK) return 0;
+  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
   if (n_splits < 1 || n_splits > kMaxSplits) return 0;
   return splitkv_workspace(B, Hq, N, d, n_splits);
 }
@@ -126,7 +127,7 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale, int n_splits,
                    hipStream_t stream) {
-  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
   if (st != FA_OK) return st;
   if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   if (B == 0 || N == 0) return FA_OK;
@@ -204,7 +205,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, bad size, flag or scale)";
-    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 64/128, or device is not gfx950)";
+    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 64/128, or 256 outside the bf16 forward; or device is not gfx950)";
     case FA_ERR_DEVICE: return "no usable HIP device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_INTERNAL: return "internal error";

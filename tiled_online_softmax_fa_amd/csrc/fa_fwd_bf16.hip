@@ -69,11 +69,17 @@ template <int D>
 struct KVSwizzle {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks16 = kRowBytes / 16;        // 16-byte chunks per row
-  static constexpr int kRowsPer256 = 256 / kRowBytes;     // rows sharing one 256-byte bank sweep
+  static constexpr int kRowsPer256 = kRowBytes >= 256 ? 1 : 256 / kRowBytes;  // rows sharing one 256-byte bank sweep
+  // XOR masks span one 256-byte sweep (16 chunks of 16 bytes, 8 of 32 bytes) at most
+  static constexpr int kKMod = kChunks16 < 16 ? kChunks16 : 16;
+  static constexpr int kVMod = kChunks16 / 2 < 8 ? kChunks16 / 2 : 8;
   // K: physical 16-byte chunk = logical chunk ^ k_swz(row)
-  __device__ static __forceinline__ int k_swz(int row) { return (row / kRowsPer256) % kChunks16; }
+  __device__ static __forceinline__ int k_swz(int row) { return (row / kRowsPer256) % kKMod; }
   // V: physical 32-byte chunk = logical 32-byte chunk ^ v_swz(row)
-  __device__ static __forceinline__ int v_swz(int row) { return (row / kRowsPer256) % (kChunks16 / 2); }
+  __device__ static __forceinline__ int v_swz(int row) { return (row / kRowsPer256) % kVMod; }
+  // the fragment reads add whole 16-row blocks to a lane's row: the masks
+  // must repeat every 16 rows
+  static_assert(16 % (kRowsPer256 * kKMod) == 0 && 16 % (kRowsPer256 * kVMod) == 0, "swizzle period");
 };
 
 // Tuning knobs (instantiated by the launcher): QPW query rows per wave, NW
@@ -86,10 +92,11 @@ struct KVSwizzle {
 // SPLIT: the workgroup processes part blockIdx.x / (n_tiles * B * Hq) of the
 // query tile's key tiles and writes that part's O (fp32) and lse to
 // p.o_part / p.lse_part for the merge kernel, instead of O and lse.
-template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false>
+template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false, int BN = 64>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
 void fa_fwd_bf16_kernel(FwdParams p) {
-  constexpr int BM = QPW * NW, BN = 64;
+  constexpr int BM = QPW * NW;
+  static_assert(BN == 32 || BN == 64, "one or two 32-key chunks per tile");
   constexpr int OPS = 2 * (BN * D * 2 / 1024) / NW;  // copy instructions per wave per tile (K and V)
   static_assert(STAGES >= 3, "the copy of tile t+STAGES-1 is issued while tile t is read");
   constexpr int QB = QPW / 16;           // 16-query blocks per wave
@@ -135,8 +142,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int n_kv = SPLIT ? (int)(((long long)(part + 1) * n_kv_all) / p.n_splits) : n_kv_all;
   // chunks this wave processes [c_lo, n_ch), and the first one that needs an element mask
   const int n_ch_all = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
-  const int n_ch = min(n_ch_all, 2 * n_kv);
-  const int c_lo = 2 * t_lo;
+  const int n_ch = min(n_ch_all, CPT * n_kv);
+  const int c_lo = CPT * t_lo;
   const int first_mask = min(n_ch_all, CAUSAL ? min((qw0 + 1) / 32, N / 32) : N / 32);
 
   // ---- K/V tile copies (asynchronous; published by the barrier of the tile)
@@ -193,7 +200,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) v_off[db] = vrow * (2 * D) + ((db ^ Swz::v_swz(vrow)) * 32) + 8 * (L & 3);
   }
-  static_assert(D == 64 || 16 % Swz::kRowsPer256 == 0, "swizzle period");
 
   // K fragments (A operand of S^T) of chunk cc (0..CPT-1) of the K tile at kt
   auto read_k = [&](const lds_u8* kt, int cc, bf16x8 (&kf)[2][DC]) __attribute__((always_inline)) {
@@ -360,19 +366,33 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   }
   // every wave's first masked chunk is at or after F
   const int F = CAUSAL ? min(q0, N) / 32 : N / 32;
-  const int t_steady = min(n_kv - 1, F >= 1 ? (F - 1) / 2 : 0);
+  // (a tile is mask-free for every wave when its chunks, and the first chunk
+  // of the next tile, all come before F)
+  const int t_steady = min(n_kv - 1, F >= 1 ? (F - 1) / CPT : 0);
   int t = t_lo;
-  for (; t < t_steady; ++t) {
-    const lds_u8* kt = stage_base(t);
-    chunk_step(kt, 0, kt, 1, 2 * t, std::false_type{});
-    publish_next(t);
-    chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::false_type{});
-  }
-  for (; t < n_kv; ++t) {
-    const lds_u8* kt = stage_base(t);
-    if (2 * t < n_ch) chunk_step(kt, 0, kt, 1, 2 * t, std::true_type{});
-    if (t + 1 < n_kv) publish_next(t);
-    if (2 * t + 1 < n_ch) chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::true_type{});
+  if constexpr (CPT == 2) {
+    for (; t < t_steady; ++t) {
+      const lds_u8* kt = stage_base(t);
+      chunk_step(kt, 0, kt, 1, 2 * t, std::false_type{});
+      publish_next(t);
+      chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::false_type{});
+    }
+    for (; t < n_kv; ++t) {
+      const lds_u8* kt = stage_base(t);
+      if (2 * t < n_ch) chunk_step(kt, 0, kt, 1, 2 * t, std::true_type{});
+      if (t + 1 < n_kv) publish_next(t);
+      if (2 * t + 1 < n_ch) chunk_step(kt, 1, stage_base(t + 1), 0, 2 * t + 1, std::true_type{});
+    }
+  } else {
+    // one chunk per tile: chunk t reads K of tile t+1, published first
+    for (; t < t_steady; ++t) {
+      publish_next(t);
+      chunk_step(stage_base(t), 0, stage_base(t + 1), 0, t, std::false_type{});
+    }
+    for (; t < n_kv; ++t) {
+      if (t + 1 < n_kv) publish_next(t);
+      if (t < n_ch) chunk_step(stage_base(t), 0, stage_base(t + 1), 0, t, std::true_type{});
+    }
   }
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
@@ -434,23 +454,33 @@ __global__ __launch_bounds__(256) void fa_fwd_merge_kernel(FwdParams p, long lon
 }
 
 // ------------------------------------------------------------------ launch
+// Head dim 256: 16 query rows per wave (the accumulator and Q^T keep the
+// register footprint of d = 128) and 32-key tiles (a 3-stage K/V ring of
+// 96 KiB).
+template <int D>
+struct FwdCfg {
+  static constexpr int QPW = D == 256 ? 16 : 32, NW = 8, STAGES = 3, BN = D == 256 ? 32 : 64;
+};
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream) {
-  constexpr int QPW = 32, NW = 8, STAGES = 3;
+  using C = FwdCfg<D>;
   FwdParams p = p_in;
-  p.n_tiles = (p.N + QPW * NW - 1) / (QPW * NW);
+  p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, QPW, NW, true, STAGES>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, C::QPW, C::NW, true, C::STAGES, false, C::BN>), dim3(grid),
+                     dim3(C::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_split_cfg(const FwdParams& p_in, hipStream_t stream) {
-  constexpr int QPW = 32, NW = 8, STAGES = 3;
+  using C = FwdCfg<D>;
   FwdParams p = p_in;
-  p.n_tiles = (p.N + QPW * NW - 1) / (QPW * NW);
+  p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq * p.n_splits);
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, QPW, NW, true, STAGES, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, C::QPW, C::NW, true, C::STAGES, true, C::BN>), dim3(grid),
+                     dim3(C::NW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)p.B * p.Hq * p.N;
@@ -461,12 +491,14 @@ static hipError_t launch_fwd_bf16_split_cfg(const FwdParams& p_in, hipStream_t s
 }
 
 hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 256) return causal ? launch_fwd_bf16_split_cfg<256, true>(p, stream) : launch_fwd_bf16_split_cfg<256, false>(p, stream);
   if (d == 128) return causal ? launch_fwd_bf16_split_cfg<128, true>(p, stream) : launch_fwd_bf16_split_cfg<128, false>(p, stream);
   if (d == 64) return causal ? launch_fwd_bf16_split_cfg<64, true>(p, stream) : launch_fwd_bf16_split_cfg<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 256) return causal ? launch_fwd_bf16_cfg<256, true>(p, stream) : launch_fwd_bf16_cfg<256, false>(p, stream);
   if (d == 128) return causal ? launch_fwd_bf16_cfg<128, true>(p, stream) : launch_fwd_bf16_cfg<128, false>(p, stream);
   if (d == 64) return causal ? launch_fwd_bf16_cfg<64, true>(p, stream) : launch_fwd_bf16_cfg<64, false>(p, stream);
   return hipErrorInvalidValue;
