@@ -180,6 +180,40 @@ def time_configs(torch, min_warmup_s):
             print(json.dumps({"workload": w.name, "entry": "fa_fwd_splitkv" if splits else "fa_fwd", "n_splits": splits,
                               "avg_us": us, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
                               "source_digest": source_digest()}), flush=True)
+
+    # backward at head dim 256 (the backward at d = 128 is the headline line): both kernels timed on their own
+    for B, H, N, d, causal in ((2, 16, 4096, 256, True),):
+        w = Workload(f"bwd_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9,
+                     backward=True)
+        inp = make_workload_inputs(w)
+        dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+               for n in ("q", "k", "v", "dO")}
+        o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        dq, dk, dv = (torch.empty_like(dev[n]) for n in ("q", "k", "v"))
+        ws = torch.empty(fa.bwd_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda:0")
+        K = 20
+        evs = [(ctypes.c_void_p * 3)(*[hip.event() for _ in range(3)]) for _ in range(K)]
+        run = lambda ev=None: fa.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["dO"], causal=causal, dq=dq, dk=dk,
+                                     dv=dv, workspace=ws, events=ev)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 10 or time.perf_counter() - t0 < min(min_warmup_s, 1.0):
+            run()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        for i in range(K):
+            run(evs[i])
+        torch.cuda.synchronize()
+        dq_us = sum(hip.ms(e[0], e[1]) for e in evs) / K * 1e3
+        dkdv_us = sum(hip.ms(e[1], e[2]) for e in evs) / K * 1e3
+        _, f_bwd = flops(B, H, N, d, causal)
+        tflops = f_bwd / ((dq_us + dkdv_us) * 1e-6) / 1e12
+        print(json.dumps({"workload": w.name, "entry": "fa_bwd", "avg_us": dq_us + dkdv_us, "dq_us": dq_us,
+                          "dkdv_us": dkdv_us, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+                          "dkdv_frac_of_peak": f_bwd * 0.8 / (dkdv_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                          "source_digest": source_digest()}), flush=True)
     return 0
 
 
@@ -292,8 +326,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM byte counters)")
     ap.add_argument("--configs", action="store_true",
-                    help="only time the forward on every forward workload of fa_inputs.WORKLOADS "
-                         "(one JSON line each; not the headline line)")
+                    help="only time the forward on every forward workload of fa_inputs.WORKLOADS, on head dim "
+                         "256 and split-KV shapes, and the backward at head dim 256 (one JSON line each; not the "
+                         "headline line)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs "
                          "of a short bench run and of a --copy-calibration run (no GPU needed)")

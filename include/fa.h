@@ -105,7 +105,7 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, contents ignored on entry (float32 scratch for the row
  * term D_i = sum_c dout_ic o_ic). All three outputs are bitwise repeatable
- * (no atomics). Supported d: 64, 128. */
+ * (no atomics). Supported d: 64, 128, 256. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,

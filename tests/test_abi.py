@@ -87,8 +87,8 @@ def test_backward_argument_errors():
         return lib.fa_bwd(*p, wsb, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], NULL)
 
     assert call(d=80) == UNS
-    assert call(d=256) == UNS
-    assert lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 256) == 0
+    assert call(d=256, ptrs=[NULL] * 10) == INV  # d = 256 is supported: validation reaches the pointers
+    assert lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 256) >= 2 * 8 * 4
     assert call(Hq=4, Hkv=3) == INV
     assert call(wsb=ws - 1) == INV
     assert call(ptrs=[BAD] * 9 + [NULL]) == INV

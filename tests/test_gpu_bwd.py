@@ -50,6 +50,13 @@ SMALL = [
     (1, 1, 1, 1, 128, True),
     (1, 2, 2, 17, 64, False),
     (1, 2, 2, 1000, 128, True),
+    # head dim 256 (64-key and 32-query tiles in dK/dV, 128-query tiles in dQ)
+    (1, 2, 2, 300, 256, False),
+    (1, 2, 2, 300, 256, True),
+    (2, 4, 2, 257, 256, True),
+    (1, 4, 1, 130, 256, False),
+    (1, 1, 1, 1, 256, True),
+    (1, 2, 2, 65, 256, True),
 ]
 
 
@@ -90,6 +97,25 @@ def test_bwd_workload_causal_4096():
     assert np.abs(sdk).max() <= 2e-2 * np.abs(dk).max() * 64
 
 
+def test_bwd_d256_causal_4096():
+    # B2 H16 N4096 d256 causal: full oracle on 2 heads, the same invariants on all heads
+    from fa_inputs import Workload
+
+    w = Workload("bwd_causal_bf16_b2h16n4096d256", 2, 16, 16, 4096, 256, "bf16", True, backward=True, seed=61)
+    _say(f"workload {w.name}: full oracle on 2 heads, invariants on all heads")
+    inp = make_workload_inputs(w)
+    dq, dk, dv = (to_f64(t) for t in _run(inp, w.causal, w.scale))
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all()
+    for b, h in ((0, 3), (1, 12)):
+        ref = attention_bwd_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], inp["dO"][b, h], w.causal, w.scale)
+        _check_grads((dq[b, h], dk[b, h], dv[b, h]), ref, f"head ({b},{h})")
+    dO = inp["dO"].astype(np.float64)
+    sdv = dv.sum(axis=2)
+    np.testing.assert_allclose(sdv, dO.sum(axis=2), atol=2e-2 * np.abs(sdv).max() + 0.25)
+    assert np.abs(dk.sum(axis=2)).max() <= 2e-2 * np.abs(dk).max() * 64
+
+
 def test_bwd_gqa_medium():
     _say("bwd GQA B1 Hq8 Hkv2 N777 d128 causal")
     inp = make_inputs(1, 8, 2, 777, 128, "bf16", seed=31, backward=True)
@@ -98,11 +124,12 @@ def test_bwd_gqa_medium():
     _check_grads(got, ref, "bwd gqa")
 
 
-def test_bwd_bitwise_repeatable():
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_bitwise_repeatable(d):
     # no atomics anywhere in the backward: every output is bitwise repeatable
-    inp = make_inputs(1, 4, 4, 600, 128, "bf16", seed=41, backward=True)
-    a = _run(inp, True, 128 ** -0.5)
-    b = _run(inp, True, 128 ** -0.5)
+    inp = make_inputs(1, 4, 4, 600, d, "bf16", seed=41, backward=True)
+    a = _run(inp, True, d ** -0.5)
+    b = _run(inp, True, d ** -0.5)
     torch = torch_mod()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
 

@@ -19,7 +19,7 @@ std::atomic<int> g_arch_state[kMaxDevices];
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shapes common to forward and backward. Returns FA_OK, or the error code.
-// Head dims: 64 and 128 everywhere, 256 where `d256` (the bf16 forward).
+// Head dims: 64 and 128 everywhere, 256 where `d256` (every bf16 entry point).
 int check_shapes(int B, int Hq, int Hkv, int N, int d, int causal, float scale, bool d256 = false) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
@@ -154,14 +154,14 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
-  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f) != FA_OK) return 0;
+  if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
   return bwd_workspace(B, Hq, N, d);
 }
 
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N,
                  int d, int causal, float scale, hipStream_t stream, hipEvent_t* events) {
-  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale);
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
   if (st != FA_OK) return st;
   if (B == 0 || N == 0) return FA_OK;
   st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace});
@@ -205,7 +205,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, bad size, flag or scale)";
-    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 64/128, or 256 outside the bf16 forward; or device is not gfx950)";
+    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 64/128/256, or 256 with fp32 storage; or device is not gfx950)";
     case FA_ERR_DEVICE: return "no usable HIP device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_INTERNAL: return "internal error";

@@ -39,23 +39,33 @@ namespace fa {
 // at chunk c ^ f(r), with f chosen so that both access patterns spread over
 // the banks: f maps the 8 (16) consecutive rows of a row-wise read to
 // distinct chunks, and the rows 4g..4g+3 of a transposed read (two adjacent
-// chunks each) to 8 distinct chunks.
+// chunks each) to 8 distinct chunks. f < 16 only permutes chunks inside one
+// 256-byte bank sweep, so with 512-byte rows (d = 256) chunk c + 16 sits
+// 256 bytes after chunk c: the fragment offsets of the second half of a row
+// are those of the first plus 256 (kHalfRow below), a constant.
 template <int D>
 struct DualSwizzle {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = kRowBytes / 16;
   __device__ static __forceinline__ int f(int row) {
     int x = ((row & 3) << 1) | ((row >> 2) & 1);
-    if (kChunks == 16) x |= ((row >> 3) & 1) << 3;
+    if (kChunks >= 16) x |= ((row >> 3) & 1) << 3;
     return x;
   }
+  // lane offsets kept per 32-column step (row-wise reads) and per 16-column
+  // block (transposed reads) within one 256-byte half row
+  static constexpr int kDC = D / 32 < 4 ? D / 32 : 4;
+  static constexpr int kDB = D / 16 < 8 ? D / 16 : 8;
+  __device__ static __forceinline__ int r_half(int dc) { return (dc / kDC) * 256; }
+  __device__ static __forceinline__ int t_half(int db) { return (db / kDB) * 256; }
 };
 
 // ------------------------------------------------------------------ kernel 2: dK, dV
 //
-// One workgroup of 8 waves per (key tile of 128 keys, batch * key/value
-// head). The waves form 4 pairs; pair p owns keys kv0 + 32p .. +31 and its two
-// waves share one SIMD (waves p and p + 4):
+// One workgroup of 8 waves per (key tile of 128 keys, 64 at d = 256,
+// batch * key/value head). The waves form 4 pairs; pair p owns keys
+// kv0 + KPW p .. + KPW - 1 (KPW = 32, 16 at d = 256) and its two waves share
+// one SIMD (waves p and p + 4):
 //   wave A (p):     S = Q K^T, P = 2^(c S - lse log2 e) (masked), dV^T += dO^T P
 //   wave B (p + 4): dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
 // so each wave keeps one of K^T / V^T and one accumulator in registers.
@@ -64,7 +74,7 @@ struct DualSwizzle {
 // operands dO^T, Q^T are transposing LDS reads of the row-major tiles.
 // Wave A hands P (bf16) to wave B through LDS; wave B runs one query tile
 // behind, so one workgroup barrier per tile publishes both the next Q/dO
-// tile and the previous tile's P. Query tiles of 64 rows (Q, dO, lse, D)
+// tile and the previous tile's P. Query tiles of 64 rows (32 at d = 256; Q, dO, lse, D)
 // stream through a 3-stage ring of asynchronous copies: at step s tile s is
 // read by A, tile s-1 by B, and the stage of tile s-2 receives tile s+1.
 // For grouped heads the sequence of tiles covers every query head of the
@@ -72,8 +82,9 @@ struct DualSwizzle {
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NP = 4, KPW = 32, BNK = NP * KPW;  // 128 keys per workgroup
-  constexpr int BMQ = 64, STAGES = 3;             // query rows per tile
+  constexpr int NP = 4, KPW = D == 256 ? 16 : 32, BNK = NP * KPW;  // keys per workgroup
+  constexpr int BMQ = D == 256 ? 32 : 64, STAGES = 3;             // query rows per tile
+  constexpr int CPQ = BMQ / 32;                                   // 32-row chunks per query tile
   constexpr int KB = KPW / 16, QB = 2, DC = D / 32, DB = D / 16;
   constexpr int RB = 2 * D;
   constexpr int QT_BYTES = BMQ * RB;                       // one Q (or dO) tile
@@ -83,7 +94,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int PIECES_PER_WAVE = PIECES / 8;
   constexpr int ROWS_PER_PIECE = 1024 / RB;
   constexpr int CH = RB / 16;
-  constexpr int P_BYTES = 2 * 2 * 64 * 16;                 // one pair's P of one tile: 2 chunks x 2 halves
+  constexpr int P_BYTES = CPQ * KB * 64 * 16;              // one pair's P of one tile: chunks x key blocks
+  constexpr int LPW = BMQ / NP;                            // lse (D) rows copied per wave
   using Swz = DualSwizzle<D>;
   static_assert(PIECES % 8 == 0 && PIECES_PER_WAVE >= 1, "copy split");
   static_assert(STAGE_BYTES % 256 == 0, "stage alignment");
@@ -128,11 +140,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const void* base = which ? (const void*)((const __bf16*)p.dout + qh * D) : (const void*)((const __bf16*)p.q + qh * D);
       copy16_global_to_lds_async(base, (uint32_t)(grow * D + lch * 8) * 2, dst + which * QT_BYTES + pp * 1024);
     }
-    // lse (waves 0-3) or D (waves 4-7): 16 rows per wave, one dword per lane
-    if (lane < 16) {
-      const int row = min(tq * BMQ + 16 * pair + lane, N - 1);
+    // lse (waves 0-3) or D (waves 4-7): LPW rows per wave, one dword per lane
+    if (lane < LPW) {
+      const int row = min(tq * BMQ + LPW * pair + lane, N - 1);
       const float* src = (role == 0 ? p.lse : p.delta) + qh;
-      copy4_global_to_lds_async(src, (uint32_t)row * 4, dst + (role == 0 ? LSE_OFF : DEL_OFF) + 64 * pair);
+      copy4_global_to_lds_async(src, (uint32_t)row * 4, dst + (role == 0 ? LSE_OFF : DEL_OFF) + 4 * LPW * pair);
     }
   };
   constexpr int OPS = PIECES_PER_WAVE + 1;  // copy instructions per wave per tile
@@ -161,17 +173,19 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   const float c = p.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
-  int r_off[DC];  // row-wise read: row L of a 16-row block, chunk dc*4 + g
+  int r_off[Swz::kDC];  // row-wise read: row L of a 16-row block, chunk dc*4 + g
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
-  int t_off[DB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
+  for (int dc = 0; dc < Swz::kDC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
+  int t_off[Swz::kDB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
   {
     const int trow = 4 * g + (L >> 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < Swz::kDB; ++db)
       t_off[db] = trow * RB + (((2 * db + ((L & 3) >> 1)) ^ Swz::f(trow)) << 4) + 8 * (L & 1);
   }
-  // P buffer of this pair: [tile parity][chunk][half][lane] x 16 bytes
+  auto roff = [&](int dc) __attribute__((always_inline)) { return r_off[dc % Swz::kDC] + Swz::r_half(dc); };
+  auto toff = [&](int db) __attribute__((always_inline)) { return t_off[db % Swz::kDB] + Swz::t_half(db); };
+  // P buffer of this pair: [tile parity][chunk][key block][lane] x 16 bytes
   lds_u8* const pbuf = smem + STAGES * STAGE_BYTES + pair * 2 * P_BYTES + lane * 16;
 
   // ---- one step: wait for tile s, publish it (and P of tile s-1), refill
@@ -202,7 +216,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bf16x8 a = lds_read_b128(qt + (cc * 32 + qb * 16) * RB + r_off[dc]);
+        const bf16x8 a = lds_read_b128(qt + (cc * 32 + qb * 16) * RB + roff(dc));
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], s[qb][kb]);
       }
@@ -230,12 +244,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) *(FA_LDS u32x4*)(pb + (cc * 2 + kb) * 1024) = pw[kb];
+    for (int kb = 0; kb < KB; ++kb) *(FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024) = pw[kb];
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4 lo4 = lds_read_tr16_b64(dt + cc * 32 * RB + t_off[db]);
-      const i16x4 hi4 = lds_read_tr16_b64(dt + (cc * 32 + 16) * RB + t_off[db]);
+      const i16x4 lo4 = lds_read_tr16_b64(dt + cc * 32 * RB + toff(db));
+      const i16x4 hi4 = lds_read_tr16_b64(dt + (cc * 32 + 16) * RB + toff(db));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, pw[kb]), acc[db][kb]);
@@ -257,7 +271,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bf16x8 a = lds_read_b128(dt + (cc * 32 + qb * 16) * RB + r_off[dc]);
+        const bf16x8 a = lds_read_b128(dt + (cc * 32 + qb * 16) * RB + roff(dc));
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], dp[qb][kb]);
       }
@@ -265,7 +279,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     u32x4 dw[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 pw = *(const FA_LDS u32x4*)(pb + (cc * 2 + kb) * 1024);
+      const u32x4 pw = *(const FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const f32x4 d4 = *(const FA_LDS f32x4*)(st + DEL_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
@@ -285,8 +299,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4 lo4 = lds_read_tr16_b64(qt + cc * 32 * RB + t_off[db]);
-      const i16x4 hi4 = lds_read_tr16_b64(qt + (cc * 32 + 16) * RB + t_off[db]);
+      const i16x4 lo4 = lds_read_tr16_b64(qt + cc * 32 * RB + toff(db));
+      const i16x4 hi4 = lds_read_tr16_b64(qt + (cc * 32 + 16) * RB + toff(db));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, dw[kb]), acc[db][kb]);
@@ -299,27 +313,28 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   if (role == 0) {
     // wave A: steps 0 .. n_seq-1 process tile s; a last step keeps the
-    // barrier count equal to wave B's. Per head: the first two tiles (the
-    // diagonal under causal) and a partial last tile take the masked path.
-    const int t_clean0 = CAUSAL ? t_first + 2 : 0;  // first tile no wave of the workgroup masks
-    const int t_clean1 = N / BMQ;                   // end of the full tiles
+    // barrier count equal to wave B's. Per head: the tiles that reach above
+    // the workgroup's last key (the diagonal under causal) and a partial
+    // last tile take the masked path.
+    const int t_clean0 = CAUSAL ? t_first + (BNK + BMQ - 2) / BMQ : 0;  // first tile no wave of the workgroup masks
+    const int t_clean1 = N / BMQ;                                        // end of the full tiles
     int s = 0;
     for (int gi = 0; gi < G; ++gi) {
       int tq = t_first;
       for (; tq < min(t_clean0, nq); ++tq, ++s) {
         begin_step(s);
-        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::true_type{});
-        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::true_type{});
+#pragma unroll
+        for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::true_type{});
       }
       for (; tq < t_clean1; ++tq, ++s) {
         begin_step(s);
-        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::false_type{});
-        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::false_type{});
+#pragma unroll
+        for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::false_type{});
       }
       for (; tq < nq; ++tq, ++s) {
         begin_step(s);
-        chunk_a(stage_of(s), tq * BMQ, 0, pbuf_of(s), std::true_type{});
-        chunk_a(stage_of(s), tq * BMQ, 1, pbuf_of(s), std::true_type{});
+#pragma unroll
+        for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::true_type{});
       }
     }
     if (n_seq > 0) begin_step(n_seq);
@@ -328,8 +343,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     if (n_seq > 0) begin_step(0);
     for (int s = 1; s <= n_seq; ++s) {
       begin_step(s);
-      chunk_b(stage_of(s - 1), 0, pbuf_of(s - 1));
-      chunk_b(stage_of(s - 1), 1, pbuf_of(s - 1));
+#pragma unroll
+      for (int cc = 0; cc < CPQ; ++cc) chunk_b(stage_of(s - 1), cc, pbuf_of(s - 1));
     }
   }
 
@@ -352,19 +367,21 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ kernel 1: dQ (and D)
 //
-// One workgroup of 8 waves per (query tile of 256 rows, batch * query head);
-// each wave owns 32 query rows. Per 32-key chunk, with keys on the
+// One workgroup of 8 waves per (query tile of 256 rows, 128 at d = 256,
+// batch * query head); each wave owns 32 query rows (16 at d = 256). Per
+// 32-key chunk, with keys on the
 // accumulator rows and queries on its columns (as in the forward kernel):
 //   S^T = K Q^T, dP^T = V dO^T                         (A: K, V rows from LDS)
 //   P^T = 2^(c S^T - lse log2 e), dS^T = P^T o (dP^T - D)   (per lane: one query)
 //   dQ^T += K^T dS^T          (A: transposing reads of the K tile, B: dS^T packed)
-// dQ = scale * dQ^T at the end. K/V tiles of 64 keys stream through a ring of
-// STAGES stages with asynchronous direct copies, one barrier per tile.
+// dQ = scale * dQ^T at the end. K/V tiles of 64 keys (32 at d = 256) stream
+// through a ring of STAGES stages with asynchronous direct copies, one
+// barrier per tile.
 template <int D, bool CAUSAL, int STAGES = 3>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int QPW = 32, NW = 8, BM = QPW * NW, BN = 64;
-  constexpr int QB = QPW / 16, DC = D / 32, DB = D / 16;
+  constexpr int QPW = D == 256 ? 16 : 32, NW = 8, BM = QPW * NW, BN = D == 256 ? 32 : 64;
+  constexpr int QB = QPW / 16, DC = D / 32, DB = D / 16, CPT = BN / 32;
   constexpr int RB = 2 * D;  // bytes per tile row
   constexpr int TILE_BYTES = BN * RB;
   constexpr int COPIES_PER_WAVE = TILE_BYTES / 1024 / NW;
@@ -395,7 +412,6 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int n_kv = (kv_end + BN - 1) / BN;
   const int n_ch = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + 31) / 32 : 0;
-  const int first_mask = min(n_ch, CAUSAL ? min(qw0 / 32, N / 32) : N / 32);
 
   auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
     const int kv0 = t * BN;
@@ -448,16 +464,18 @@ void fa_bwd_dq_kernel(BwdParams p) {
   for (int qb = 0; qb < QB; ++qb) lim[qb] = (CAUSAL ? min(qw0 + qb * 16 + L, N - 1) : N - 1) - 4 * g;
 
   // lane parts of the LDS fragment offsets
-  int r_off[DC];  // row L of a 16-row block, chunk dc*4 + g
+  int r_off[Swz::kDC];  // row L of a 16-row block, chunk dc*4 + g
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
-  int t_off[DB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
+  for (int dc = 0; dc < Swz::kDC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
+  int t_off[Swz::kDB];  // transposed read: row 4g + L/4 of a 32-row chunk, columns 16 db + 4 (L & 3) .. +3
   {
     const int trow = 4 * g + (L >> 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < Swz::kDB; ++db)
       t_off[db] = trow * RB + (((2 * db + ((L & 3) >> 1)) ^ Swz::f(trow)) << 4) + 8 * (L & 1);
   }
+  auto roff = [&](int dc) __attribute__((always_inline)) { return r_off[dc % Swz::kDC] + Swz::r_half(dc); };
+  auto toff = [&](int db) __attribute__((always_inline)) { return t_off[db % Swz::kDB] + Swz::t_half(db); };
 
   // One 32-key chunk (K rows at kt, V rows at kt + TILE_BYTES, chunk index ch).
   auto chunk = [&](const lds_u8* kt, int ch, auto mask) __attribute__((always_inline)) {
@@ -472,8 +490,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
         bf16x8 kf[DC], vf[DC];
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          kf[dc] = lds_read_b128(kt + hb * 16 * RB + r_off[dc]);
-          vf[dc] = lds_read_b128(vt + hb * 16 * RB + r_off[dc]);
+          kf[dc] = lds_read_b128(kt + hb * 16 * RB + roff(dc));
+          vf[dc] = lds_read_b128(vt + hb * 16 * RB + roff(dc));
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -513,8 +531,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4 lo = lds_read_tr16_b64(kt + t_off[db]);
-      const i16x4 hi = lds_read_tr16_b64(kt + 16 * RB + t_off[db]);
+      const i16x4 lo = lds_read_tr16_b64(kt + toff(db));
+      const i16x4 hi = lds_read_tr16_b64(kt + 16 * RB + toff(db));
       const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma_bf16_16x16x32(ka, dsf[qb], acc[db][qb]);
@@ -546,14 +564,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
   int t = 0;
   for (; t < t_mask; ++t) {
     const lds_u8* kt = begin_tile(t);
-    chunk(kt, 2 * t, std::false_type{});
-    chunk(kt + 32 * RB, 2 * t + 1, std::false_type{});
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) chunk(kt + cc * 32 * RB, CPT * t + cc, std::false_type{});
   }
   for (; t < n_kv; ++t) {
     const lds_u8* kt = begin_tile(t);
-    const int ch0 = 2 * t;
-    if (ch0 < n_ch) chunk(kt, ch0, std::true_type{});
-    if (ch0 + 1 < n_ch) chunk(kt + 32 * RB, ch0 + 1, std::true_type{});
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc)
+      if (CPT * t + cc < n_ch) chunk(kt + cc * 32 * RB, CPT * t + cc, std::true_type{});
   }
 
   // dQ = scale * dQ^T: lane holds query L + 16 qb, d = 16 db + 4 g + r
@@ -575,15 +593,16 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------ launch
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipEvent_t* ev) {
+  constexpr int BM_DQ = D == 256 ? 128 : 256, BN_DKDV = D == 256 ? 64 : 128;  // as in the kernels
   BwdParams p = p_in;
   hipError_t e;
   // dQ first: it also writes the row term D that the dK/dV kernel reads
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  p.n_tiles = (p.N + 255) / 256;
+  p.n_tiles = (p.N + BM_DQ - 1) / BM_DQ;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  p.n_tiles = (p.N + 127) / 128;
+  p.n_tiles = (p.N + BN_DKDV - 1) / BN_DKDV;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(512), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -592,6 +611,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* ev) {
+  if (d == 256) return causal ? launch_bwd_cfg<256, true>(p, stream, ev) : launch_bwd_cfg<256, false>(p, stream, ev);
   if (d == 128) return causal ? launch_bwd_cfg<128, true>(p, stream, ev) : launch_bwd_cfg<128, false>(p, stream, ev);
   if (d == 64) return causal ? launch_bwd_cfg<64, true>(p, stream, ev) : launch_bwd_cfg<64, false>(p, stream, ev);
   return hipErrorInvalidValue;
