@@ -7,6 +7,8 @@ CPU-baseline leg use it. It shares no code with the HIP path.
 * ``attention``: the plain definition, softmax(scale * q k^T) v, with the full
   score matrix materialised in float64, its row logsumexp, and the gradients
   obtained from the calculus of that definition.
+* ``blocksparse``: the definition restricted to the (query block, key block)
+  pairs a block mask enables, in float64.
 * ``online``: the tiled online-softmax recurrence in its two published forms
   (normalise every block; defer the normalisation to the end), in float64,
   written from the pages' description. It exists to check that tiling reaches
@@ -24,6 +26,7 @@ from .attention import (
     attention_bwd_head,
     causal_tile_count,
 )
+from .blocksparse import attention_fwd_blockmask, element_mask
 from .online import online_fwd_normalise_each_block, online_fwd_deferred
 
 __all__ = [
@@ -33,6 +36,8 @@ __all__ = [
     "attention_bwd",
     "attention_bwd_head",
     "causal_tile_count",
+    "attention_fwd_blockmask",
+    "element_mask",
     "online_fwd_normalise_each_block",
     "online_fwd_deferred",
 ]
