@@ -181,6 +181,53 @@ def time_configs(torch, min_warmup_s):
                               "avg_us": us, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
                               "source_digest": source_digest()}), flush=True)
 
+    # block-sparse forward (128 x 128 mask blocks): work counted over the visible (query, key) pairs only
+    from fa_inputs import make_block_mask
+
+    def visible_pairs(m, N, block, causal):
+        """(query, key) pairs a [n_blk, n_blk] block mask lets through (with the causal mask if set)."""
+        n = m.shape[0]
+        sz = np.array([min(block, N - i * block) for i in range(n)], dtype=np.int64)
+        pairs = np.outer(sz, sz)
+        if causal:
+            lower = np.tril(np.ones((n, n), bool), -1)
+            pairs = np.where(lower, pairs, 0) + np.diag(sz * (sz + 1) // 2)
+        return int((m.astype(np.int64) * pairs).sum())
+
+    for B, H, N, d, causal, kind in ((2, 16, 4096, 128, True, "band"), (2, 16, 4096, 128, False, "band"),
+                                     (2, 16, 4096, 128, False, "random")):
+        w = Workload(f"blocksparse_{kind}_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16",
+                     causal, seed=9)
+        inp = make_workload_inputs(w)
+        dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+               for n in ("q", "k", "v")}
+        mask = make_block_mask(kind, B, H, N, seed=1)
+        visible = sum(visible_pairs(mask[b, h], N, 128, causal) for b in range(B) for h in range(H))
+        m_dev = torch.from_numpy(mask).to("cuda:0")
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        run = lambda: fa.fwd_blocksparse(dev["q"], dev["k"], dev["v"], m_dev, causal=causal, out=o, lse=lse)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 10 or time.perf_counter() - t0 < min(min_warmup_s, 0.5):
+            run()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(20):
+            run()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        us = hip.ms(e0, e1) / 20 * 1e3
+        f_vis = 4.0 * d * visible
+        tflops = f_vis / (us * 1e-6) / 1e12
+        print(json.dumps({"workload": w.name, "entry": "fa_fwd_blocksparse", "mask": kind,
+                          "visible_fraction": visible / (B * H * N * N), "avg_us": us, "tflops": tflops,
+                          "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "source_digest": source_digest()}), flush=True)
+
     # backward at head dim 256 (the backward at d = 128 is the headline line): both kernels timed on their own
     for B, H, N, d, causal in ((2, 16, 4096, 256, True),):
         w = Workload(f"bwd_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9,
@@ -327,8 +374,8 @@ def main():
                     help="only run a plain device copy of known size (for scaling the HBM byte counters)")
     ap.add_argument("--configs", action="store_true",
                     help="only time the forward on every forward workload of fa_inputs.WORKLOADS, on head dim "
-                         "256 and split-KV shapes, and the backward at head dim 256 (one JSON line each; not the "
-                         "headline line)")
+                         "256, split-KV and block-sparse shapes, and the backward at head dim 256 (one JSON line "
+                         "each; not the headline line)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs "
                          "of a short bench run and of a --copy-calibration run (no GPU needed)")

@@ -24,6 +24,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "bf16_round",
     "make_inputs",
+    "make_block_mask",
 ]
 
 
@@ -125,3 +126,30 @@ def make_inputs(B, Hq, Hkv, N, d, dtype="bf16", seed=0, backward=False, q_mult=1
 
 def make_workload_inputs(w: Workload, q_mult=1.0):
     return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.backward, q_mult)
+
+
+def make_block_mask(kind, B, Hq, N, seed=0, block=128):
+    """A block mask [B, Hq, n_blk, n_blk] (uint8, 1 = the query block sees the key block), n_blk = ceil(N / block).
+
+    kinds: "all" (every block), "diag" (block i sees block i), "band" (blocks
+    i-1, i, i+1 and the first block: a sliding window plus one global block),
+    "random" (each entry 1 with probability 1/2, seeded, differing per batch
+    and head), "holes" ("random" with every third query block seeing nothing).
+    """
+    n = -(-N // block)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    if kind == "all":
+        m = np.ones((n, n), bool)
+    elif kind == "diag":
+        m = i == j
+    elif kind == "band":
+        m = (np.abs(i - j) <= 1) | (j == 0)
+    elif kind in ("random", "holes"):
+        m = np.random.default_rng(seed).random((B, Hq, n, n)) < 0.5
+        if kind == "holes":
+            m[:, :, ::3, :] = False
+        return m.astype(np.uint8)
+    else:
+        raise ValueError(f"unknown block mask kind {kind!r}")
+    return np.ascontiguousarray(np.broadcast_to(m, (B, Hq, n, n))).astype(np.uint8)

@@ -95,6 +95,30 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    int n_splits, hipStream_t stream);
 
+/* Block size (queries and keys) of the block mask of fa_fwd_blocksparse, and
+ * the largest N it accepts (1024 blocks). */
+#define FA_SPARSE_BLOCK 128
+#define FA_SPARSE_MAX_N 131072
+
+/* Forward attention, bf16, restricted by a block mask: the query rows and
+ * the keys are cut into blocks of FA_SPARSE_BLOCK (the last one ragged),
+ * n_blk = ceil(N / FA_SPARSE_BLOCK), and key j is visible to query i iff
+ * the mask entry of (i / FA_SPARSE_BLOCK, j / FA_SPARSE_BLOCK) is non-zero
+ * (and j <= i when causal). Key blocks that no query of a workgroup sees are
+ * never loaded (the block-sparse integration of "FlashAttention技术解析"
+ * (mhpq.cn), section 6.2; each query row takes one softmax over all the keys
+ * it sees). A row that sees no key gets o = 0 and lse = -inf.
+ * block_mask: device uint8, caller-owned; the entry (b, h, qb, kb) for query
+ * head h is block_mask[b * mask_stride_b + h * mask_stride_h + qb * n_blk + kb]
+ * (strides in bytes, >= 0; 0 shares one mask across batches or heads), so
+ * each [n_blk, n_blk] mask is row-major and contiguous.
+ * Other arguments, layouts and limits as fa_fwd, plus N <= FA_SPARSE_MAX_N
+ * (FA_ERR_UNSUPPORTED beyond) and negative strides FA_ERR_INVALID_ARG. */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const unsigned char* block_mask, long long mask_stride_b, long long mask_stride_h,
+                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       hipStream_t stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (0 on invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

@@ -25,8 +25,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_f32",
-                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd",
+                                    "fa_fwd_blocksparse", "fa_fwd_f32", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -122,6 +123,29 @@ def test_splitkv_argument_errors():
     assert call(ptrs=[BAD] * 5 + [NULL]) == INV
     assert call(Hq=3, Hkv=2) == INV
     assert call(B=0, ptrs=[NULL] * 6, wsb=0) == FA_OK
+
+
+def test_blocksparse_argument_errors():
+    from tiled_online_softmax_fa_amd import FA_ERR_INVALID_ARG as INV, FA_ERR_UNSUPPORTED as UNS, FA_OK
+
+    lib = _lib()
+
+    def call(ptrs=None, mask=BAD, sb=0, sh=0, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125)
+        a.update(kw)
+        p = ptrs or [BAD] * 5
+        return lib.fa_fwd_blocksparse(*p, mask, sb, sh, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                      a["scale"], NULL)
+
+    assert call(d=96) == UNS
+    assert call(N=131073) == UNS
+    assert call(sb=-1) == INV
+    assert call(sh=-128) == INV
+    assert call(Hq=3, Hkv=2) == INV
+    assert call(mask=NULL) == INV
+    assert call(ptrs=[BAD, BAD, BAD, NULL, BAD]) == INV
+    assert call(d=256, ptrs=[NULL] * 5) == INV
+    assert call(B=0, ptrs=[NULL] * 5, mask=NULL) == FA_OK
 
 
 def test_status_strings():

@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_timed.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_splitkv.restype = i
+    ll = ctypes.c_longlong
+    lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, ll, ll, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_blocksparse.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -190,6 +193,57 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, out=None, lse=None,
     st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), int(n_splits), _stream_ptr(q))
     _check(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+SPARSE_BLOCK = 128  # FA_SPARSE_BLOCK
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, lse=None):
+    """Forward attention on bf16 tensors restricted by a block mask of 128 x 128 blocks.
+
+    block_mask: uint8 or bool GPU tensor [n_blk, n_blk] (shared by all batches and heads),
+    [Hq, n_blk, n_blk] (per query head) or [B, Hq, n_blk, n_blk], n_blk = ceil(N / 128);
+    the last two dims contiguous. Rows that see no key get o = 0, lse = -inf. Returns (o, lse).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n_blk = -(-N // SPARSE_BLOCK)
+    m = block_mask
+    if not isinstance(m, torch.Tensor) or not m.is_cuda or m.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("block_mask must be a uint8 or bool GPU tensor")
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if tuple(m.shape[-2:]) != (n_blk, n_blk) or m.dim() not in (2, 3, 4):
+        raise ValueError(f"block_mask must end in [{n_blk}, {n_blk}]")
+    if m.stride(-1) != 1 or m.stride(-2) != n_blk:
+        raise ValueError("block_mask's last two dims must be contiguous")
+    if m.dim() == 2:
+        sb, sh = 0, 0
+    elif m.dim() == 3:
+        if m.shape[0] != Hq:
+            raise ValueError("a 3-d block_mask is [Hq, n_blk, n_blk]")
+        sb, sh = 0, m.stride(0)
+    else:
+        if m.shape[0] != B or m.shape[1] != Hq:
+            raise ValueError("a 4-d block_mask is [B, Hq, n_blk, n_blk]")
+        sb, sh = m.stride(0), m.stride(1)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require(out, torch.bfloat16, "out")
+    _require(lse, torch.float32, "lse")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    lib = load_library()
+    st = lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(m), sb, sh, B, Hq, Hkv, N, d,
+                                int(bool(causal)), float(scale), _stream_ptr(q))
+    _check(st, "fa_fwd_blocksparse")
     return out, lse
 
 

@@ -153,6 +153,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return launch_status(fa::launch_fwd_bf16_splitkv(p, d, causal != 0, stream));
 }
 
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const unsigned char* block_mask, long long mask_stride_b, long long mask_stride_h, int B, int Hq,
+                       int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+  static_assert(FA_SPARSE_BLOCK == fa::kSparseBlock && FA_SPARSE_MAX_N == fa::kSparseMaxN, "block-mask limits");
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
+  if (st != FA_OK) return st;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  if (N > FA_SPARSE_MAX_N) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q, k, v, o, lse});
+  if (st != FA_OK) return st;
+  if (block_mask == nullptr) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.scale_log2 = scale * kLog2e;
+  p.block_mask = block_mask;
+  p.mask_stride_b = mask_stride_b;
+  p.mask_stride_h = mask_stride_h;
+  return launch_status(fa::launch_fwd_bf16_blocksparse(p, d, causal != 0, stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
   return bwd_workspace(B, Hq, N, d);

@@ -92,7 +92,16 @@ struct KVSwizzle {
 // SPLIT: the workgroup processes part blockIdx.x / (n_tiles * B * Hq) of the
 // query tile's key tiles and writes that part's O (fp32) and lse to
 // p.o_part / p.lse_part for the merge kernel, instead of O and lse.
-template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false, int BN = 64>
+// SPARSE: a block mask of 128 x 128 blocks says which key blocks each query
+// block sees ("FlashAttention技术解析" (mhpq.cn) section 6.2, block-sparse
+// integration). The workgroup first compacts the key blocks that any of its
+// query blocks sees (the union; causal drops blocks wholly above the
+// diagonal) into a list in LDS and then streams only those tiles, exactly
+// as the causal skip streams only the tiles below the diagonal. A wave
+// whose own query block does not see a listed block masks it out element
+// by element. Rows that see no key get O = 0 and lse = -inf.
+template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false, int BN = 64,
+          bool SPARSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
 void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = QPW * NW;
@@ -110,10 +119,16 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int CH = 2 * D / 16;
   using Swz = KVSwizzle<D>;
   static_assert(COPIES % NW == 0, "K/V copy must split evenly over the waves");
+  constexpr int SB = kSparseBlock;  // block-mask block (queries and keys)
+  constexpr int TPB = SB / BN;      // key tiles per mask block
+  static_assert(!SPARSE || (BM % SB == 0 && BM / SB <= 2 && !SPLIT), "sparse: 1 or 2 query blocks per workgroup");
 
   // ring of STAGES x (K tile, V tile)
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
+  // sparse: listed key blocks, bits 0-13 block index, bit 14 + i: query block i of the workgroup sees it
+  __shared__ uint16_t blk_list[SPARSE ? kSparseMaxBlocks : 1];
+  __shared__ int blk_count[SPARSE ? NW : 1];
 
   const int N = p.N;
   const int lane = threadIdx.x & 63;
@@ -135,8 +150,53 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   const int q0 = tc.tile * BM;
   const int qw0 = q0 + wave * QPW;  // first query row of this wave
+
+  // sparse: compact the listed key blocks (ballot + prefix over the waves)
+  int n_list = 0;
+  if constexpr (SPARSE) {
+    const int n_kb = (N + SB - 1) / SB;
+    const int qb0 = q0 / SB;
+    const int nqb = min(BM / SB, n_kb - qb0);
+    const unsigned char* mrow =
+        p.block_mask + (long long)b * p.mask_stride_b + (long long)h * p.mask_stride_h + (long long)qb0 * n_kb;
+    const int n_scan = CAUSAL ? min(n_kb, qb0 + nqb) : n_kb;
+    for (int j0 = 0; j0 < n_scan; j0 += NW * 64) {
+      const int j = j0 + (int)threadIdx.x;
+      bool v0 = false, v1 = false;
+      if (j < n_scan) {
+        v0 = mrow[j] != 0 && (!CAUSAL || j <= qb0);
+        v1 = nqb > 1 && mrow[n_kb + j] != 0 && (!CAUSAL || j <= qb0 + 1);
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(v0 || v1);
+      if (lane == 0) blk_count[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cnt = blk_count[w];
+        before += w < wave ? cnt : 0;
+        total += cnt;
+      }
+      if (v0 || v1) {
+        const int pos = n_list + before + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        blk_list[pos] = (uint16_t)(j | (v0 ? 1 << 14 : 0) | (v1 ? 1 << 15 : 0));
+      }
+      n_list += total;
+      __syncthreads();  // the list is complete; blk_count may be reused
+    }
+  }
+  // sparse: sequence position t -> key tile, and whether this wave's query block sees it
+  auto kv_tile_of = [&](int t) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return uniform((blk_list[t / TPB] & 0x3FFF) * TPB + t % TPB);
+    else return t;
+  };
+  const int wave_qblock = (wave * QPW) / SB;
+  auto sees_tile = [&](int t) __attribute__((always_inline)) {
+    return ((uniform(blk_list[t / TPB]) >> (14 + wave_qblock)) & 1) != 0;
+  };
+
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_kv_all = (kv_end + BN - 1) / BN;  // key tiles with a visible key for the workgroup
+  const int n_kv_all = SPARSE ? n_list * TPB : (kv_end + BN - 1) / BN;  // key tiles the workgroup visits
   // this workgroup's key tiles [t_lo, n_kv) (all of them without SPLIT)
   const int t_lo = SPLIT ? (int)(((long long)part * n_kv_all) / p.n_splits) : 0;
   const int n_kv = SPLIT ? (int)(((long long)(part + 1) * n_kv_all) / p.n_splits) : n_kv_all;
@@ -148,7 +208,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   // ---- K/V tile copies (asynchronous; published by the barrier of the tile)
   auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
-    const int kv0 = t * BN;
+    const int kv0 = kv_tile_of(t) * BN;
     const uint32_t kdst = lds_address(smem) + ((t - t_lo) % STAGES) * 2 * TILE_BYTES;
 #pragma unroll
     for (int c = 0; c < COPIES_PER_WAVE; ++c) {
@@ -233,7 +293,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     }
     if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
-  auto apply_mask = [&](int ch, f32x4 (&s)[2][QB]) __attribute__((always_inline)) {
+  auto apply_mask = [&](int ch, f32x4 (&s)[2][QB], bool sees = true) __attribute__((always_inline)) {
     const int key0 = ch * 32;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -243,7 +303,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + hb * 16 + g * 4 + r;
           const int qi = qw0 + qb * 16 + L;
-          const bool visible = key < N && (!CAUSAL || key <= qi);
+          const bool visible = (!SPARSE || sees) && key < N && (!CAUSAL || key <= qi);
           s[hb][qb][r] = visible ? s[hb][qb][r] : kNegInf;
         }
   };
@@ -281,7 +341,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   auto exponentiate = [&](const f32x4 (&s)[2][QB], bf16x8 (&pf)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = -m_ref[qb];
+      // sparse: a row may have seen no key yet (m = -inf); its masked scores give 2^-inf = 0
+      const float neg_m = (SPARSE && m_ref[qb] == kNegInf) ? 0.f : -m_ref[qb];
       float e[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -307,11 +368,11 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   f32x4 s_cur[2][QB];
 
   // S^T of chunk ch (K tile at kt, position cc), masked when MASK, and the reference update.
-  auto scores = [&](const lds_u8* kt, int cc, int ch, auto mask) __attribute__((always_inline)) {
+  auto scores = [&](const lds_u8* kt, int cc, int ch, auto mask, bool sees = true) __attribute__((always_inline)) {
     bf16x8 kf[2][DC];
     read_k(kt, cc, kf);
     compute_s(kf, s_cur);
-    if (decltype(mask)::value) apply_mask(ch, s_cur);
+    if (decltype(mask)::value) apply_mask(ch, s_cur, sees);
     float tmax[QB];
     chunk_max(s_cur, tmax);
     update_reference(tmax);
@@ -328,6 +389,37 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     exponentiate(s_cur, pf);
     accumulate_pv(vf, pf);
     if (!decltype(mask)::value || ch + 1 < n_ch) scores(ktn, ccn, ch + 1, mask);
+  };
+  // sparse: one step of this wave's own chunk sequence. A chunk the wave
+  // does not see (block off, wholly above its diagonal, or past the end) is
+  // skipped; s_cur is live (cur_live) when the previous step computed the
+  // scores of a seen chunk. Both live: the straight-line step of the dense
+  // loop (masked only where the diagonal or the end of the sequence cuts
+  // the next chunk); otherwise only the half that exists.
+  auto chunk_needs_mask = [&](int ch) __attribute__((always_inline)) {
+    const int key_last = ch * 32 + 31;
+    return (CAUSAL && key_last > qw0) || key_last >= N;
+  };
+  auto chunk_seen = [&](int ch, bool block_seen) __attribute__((always_inline)) {
+    return block_seen && ch * 32 < N && !(CAUSAL && ch * 32 > qw0 + QPW - 1);
+  };
+  auto finish_chunk = [&](const lds_u8* kt, int cc) __attribute__((always_inline)) {
+    bf16x8 vf[DB], pf[QB];
+    read_v(kt, cc, vf);
+    exponentiate(s_cur, pf);
+    accumulate_pv(vf, pf);
+  };
+  auto sparse_step = [&](const lds_u8* kt, int cc, const lds_u8* ktn, int ccn, int next_ch, bool next_live,
+                         bool& cur_live, auto mask) __attribute__((always_inline)) {
+    if (cur_live && next_live) {
+      finish_chunk(kt, cc);
+      scores(ktn, ccn, next_ch, mask);
+    } else if (cur_live) {
+      finish_chunk(kt, cc);
+    } else if (next_live) {
+      scores(ktn, ccn, next_ch, mask);
+    }
+    cur_live = next_live;
   };
 
   // ---- key loop: tiles in workgroup lock-step, chunks per wave. The last
@@ -356,7 +448,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       wait_vmcnt0();
     }
     __syncthreads();
-    if (n_ch > c_lo) {
+    if constexpr (SPARSE) {
+      // (the first chunk's scores; the loop below consumes them)
+    } else if (n_ch > c_lo) {
       if (first_mask > c_lo) {
         scores(smem, 0, c_lo, std::false_type{});
       } else {
@@ -370,7 +464,60 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // of the next tile, all come before F)
   const int t_steady = min(n_kv - 1, F >= 1 ? (F - 1) / CPT : 0);
   int t = t_lo;
-  if constexpr (CPT == 2) {
+  if constexpr (SPARSE) {
+    // Listed tiles before t_clean need no element mask in any wave (below
+    // every diagonal of the workgroup and inside the sequence; the list is
+    // in key order, so they come first): an unmasked region, then a masked
+    // one, as in the dense loop.
+    // (head dim 256: one masked region only; the second copy of the chunk
+    // code does not fit the register budget there)
+    int t_clean = 0;
+    if constexpr (D <= 128) {
+      const int clean_end = min(CAUSAL ? q0 : N, N - N % BN);  // tiles wholly before this key need no mask
+      while (t_clean < n_kv && (kv_tile_of(t_clean) + 1) * BN <= clean_end) ++t_clean;
+    }
+    bool cur_live = false;
+    auto run = [&](int t_end, auto mask) __attribute__((always_inline)) {
+      for (; t < t_end; ++t) {
+        const lds_u8* kt = stage_base(t);
+        const bool more = t + 1 < n_kv;
+        const int tile = kv_tile_of(t);
+        // the next chunk of the last tile of the unmasked region belongs to the masked one
+        const bool next_tile_clean = !decltype(mask)::value && t + 1 < t_clean;
+        if constexpr (CPT == 2) {
+          sparse_step(kt, 0, kt, 1, tile * 2 + 1, chunk_seen(tile * 2 + 1, sees_tile(t)), cur_live, mask);
+          if (more) publish_next(t);
+          const int nch = more ? kv_tile_of(t + 1) * 2 : 0;
+          const bool nl = more && chunk_seen(nch, sees_tile(t + 1));
+          if (decltype(mask)::value || next_tile_clean) {
+            sparse_step(kt, 1, stage_base(t + 1), 0, nch, nl, cur_live, mask);
+          } else {
+            sparse_step(kt, 1, stage_base(t + 1), 0, nch, nl, cur_live, std::true_type{});
+          }
+        } else {
+          if (more) publish_next(t);
+          const int nch = more ? kv_tile_of(t + 1) : 0;
+          const bool nl = more && chunk_seen(nch, sees_tile(t + 1));
+          if (decltype(mask)::value || next_tile_clean) {
+            sparse_step(kt, 0, stage_base(t + 1), 0, nch, nl, cur_live, mask);
+          } else {
+            sparse_step(kt, 0, stage_base(t + 1), 0, nch, nl, cur_live, std::true_type{});
+          }
+        }
+      }
+    };
+    if (n_kv > 0) {  // scores of the first chunk (tile 0, published above)
+      const int ch0 = kv_tile_of(0) * CPT;
+      const bool live0 = chunk_seen(ch0, sees_tile(0));
+      if (t_clean > 0) {
+        sparse_step(smem, 0, smem, 0, ch0, live0, cur_live, std::false_type{});
+      } else {
+        sparse_step(smem, 0, smem, 0, ch0, live0, cur_live, std::true_type{});
+      }
+    }
+    run(t_clean, std::false_type{});
+    run(n_kv, std::true_type{});
+  } else if constexpr (CPT == 2) {
     for (; t < t_steady; ++t) {
       const lds_u8* kt = stage_base(t);
       chunk_step(kt, 0, kt, 1, 2 * t, std::false_type{});
@@ -410,14 +557,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db) *(f32x4*)(p.o_part + prow * D + db * 16 + g * 4) = acc[db][qb] * inv;
         if (g == 0) p.lse_part[prow] = l > 0.f ? (m_ref[qb] + log2_fast(l)) * kLn2 : kNegInf;
       } else {
-        const float inv = 1.0f / l;
+        // (sparse: a row that saw no key has l = 0 and gets O = 0, lse = -inf)
+        const float inv = (!SPARSE || l > 0.f) ? 1.0f / l : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const f32x4 o4 = acc[db][qb] * inv;
           u32x2 packed = {pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
           *(u32x2*)(og + (size_t)row * D + db * 16 + g * 4) = packed;
         }
-        if (g == 0) lseg[row] = (m_ref[qb] + log2_fast(l)) * kLn2;
+        if (g == 0) lseg[row] = (!SPARSE || l > 0.f) ? (m_ref[qb] + log2_fast(l)) * kLn2 : kNegInf;
       }
     }
   }
@@ -494,6 +642,24 @@ hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int d, bool causal, hipSt
   if (d == 256) return causal ? launch_fwd_bf16_split_cfg<256, true>(p, stream) : launch_fwd_bf16_split_cfg<256, false>(p, stream);
   if (d == 128) return causal ? launch_fwd_bf16_split_cfg<128, true>(p, stream) : launch_fwd_bf16_split_cfg<128, false>(p, stream);
   if (d == 64) return causal ? launch_fwd_bf16_split_cfg<64, true>(p, stream) : launch_fwd_bf16_split_cfg<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_sparse_cfg(const FwdParams& p_in, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  FwdParams p = p_in;
+  p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
+  const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, C::QPW, C::NW, true, C::STAGES, false, C::BN, true>), dim3(grid),
+                     dim3(C::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_blocksparse(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 256) return causal ? launch_fwd_bf16_sparse_cfg<256, true>(p, stream) : launch_fwd_bf16_sparse_cfg<256, false>(p, stream);
+  if (d == 128) return causal ? launch_fwd_bf16_sparse_cfg<128, true>(p, stream) : launch_fwd_bf16_sparse_cfg<128, false>(p, stream);
+  if (d == 64) return causal ? launch_fwd_bf16_sparse_cfg<64, true>(p, stream) : launch_fwd_bf16_sparse_cfg<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

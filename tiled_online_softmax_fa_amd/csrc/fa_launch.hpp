@@ -21,6 +21,10 @@ struct FwdParams {
   int n_splits;
   float* o_part;
   float* lse_part;
+  // block-sparse only: uint8 mask, element (b, h, qb, kb) at
+  // block_mask[b * mask_stride_b + h * mask_stride_h + qb * n_blk + kb]
+  const unsigned char* block_mask;
+  long long mask_stride_b, mask_stride_h;
 };
 
 struct BwdParams {
@@ -44,6 +48,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 // split-KV forward: the partial kernel then the merge (p.n_splits >= 1, workspace in p.o_part / p.lse_part)
 hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// block-sparse forward (p.block_mask set; N <= kSparseMaxN)
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 1024;
+constexpr int kSparseMaxN = kSparseBlock * kSparseMaxBlocks;
+hipError_t launch_fwd_bf16_blocksparse(const FwdParams& p, int d, bool causal, hipStream_t stream);
 // events: NULL or 3 events recorded before/between/after the two backward kernels
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* events);
 
