@@ -143,7 +143,8 @@ def time_configs(torch, min_warmup_s):
     # vs key-range parts
     from fa_inputs import Workload
 
-    for B, H, N, d, causal, split_list in ((2, 16, 4096, 256, True, (0,)), (2, 16, 4096, 256, False, (0,)),
+    for B, H, N, d, causal, split_list in ((2, 16, 4096, 128, False, (0,)),
+                                          (2, 16, 4096, 256, True, (0,)), (2, 16, 4096, 256, False, (0,)),
                                           (1, 8, 16384, 128, True, (0, 2, 4, 8)),
                                           (1, 4, 8192, 128, False, (0, 2, 4, 8))):
         w = Workload(f"{'splitkv_' if len(split_list) > 1 else 'fwd_'}b{B}h{H}n{N}d{d}{'_causal' if causal else ''}",
