@@ -9,6 +9,8 @@ CPU-baseline leg use it. It shares no code with the HIP path.
   obtained from the calculus of that definition.
 * ``blocksparse``: the definition restricted to the (query block, key block)
   pairs a block mask enables, in float64.
+* ``fp8``: e4m3 codes from their bit fields, block-wise quantisation with one
+  float32 scale per 64 rows, and the definition on the dequantised inputs.
 * ``online``: the tiled online-softmax recurrence in its two published forms
   (normalise every block; defer the normalisation to the end), in float64,
   written from the pages' description. It exists to check that tiling reaches
@@ -27,6 +29,15 @@ from .attention import (
     causal_tile_count,
 )
 from .blocksparse import attention_fwd_blockmask, element_mask
+from .fp8 import (
+    E4M3_MAX,
+    attention_fwd_fp8,
+    dequantize_blockwise_e4m3,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_values,
+    quantize_blockwise_e4m3,
+)
 from .online import online_fwd_normalise_each_block, online_fwd_deferred
 
 __all__ = [
@@ -38,6 +49,13 @@ __all__ = [
     "causal_tile_count",
     "attention_fwd_blockmask",
     "element_mask",
+    "E4M3_MAX",
+    "attention_fwd_fp8",
+    "dequantize_blockwise_e4m3",
+    "e4m3_decode",
+    "e4m3_encode",
+    "e4m3_values",
+    "quantize_blockwise_e4m3",
     "online_fwd_normalise_each_block",
     "online_fwd_deferred",
 ]
