@@ -18,7 +18,8 @@ Readings where the pages are silent or garbled:
   for e4m3 (127 is the int8 maximum).
 * rounding: to nearest, ties to the even code; values beyond 448 saturate to
   448 (they do not occur: x / scale <= 448 by construction, up to one
-  rounding of the division).
+  rounding of the division). The sign is kept as in IEEE 754 rounding, so a
+  negative value whose magnitude rounds to zero gives -0 (code 0x80).
 * block: 64 consecutive rows of one (batch, head) across the whole head dim
   (the page's 64 x 64 block with d = 64); a block of zeros gets scale 1.
 * the scale is formed and applied in float32, as the kernels do:
@@ -78,8 +79,7 @@ def e4m3_encode(y):
     d_hi = _POS_VALUES[hi] - a
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi != lo) & (_POS_CODES[hi] % 2 == 0))
     code = np.where(take_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
-    neg = np.signbit(y) & (code != 0)
-    return np.where(neg, code | 0x80, code).astype(np.uint8)
+    return np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
 
 
 def quantize_blockwise_e4m3(x, block=64):

@@ -38,7 +38,8 @@ def test_encode_round_trip_and_ties_to_even():
     assert np.array_equal(e4m3_encode(mid + step / 8), (lower + 1).astype(np.uint8))
     assert e4m3_encode(np.array([1e6, -500.0, 460.0]))[0] == 0x7E
     assert list(e4m3_encode(np.array([-500.0, 460.0]))) == [0xFE, 0x7E]
-    assert e4m3_encode(np.array([-1e-30]))[0] == 0x00   # rounds to zero: no negative zero code
+    # the sign survives rounding to zero (IEEE 754): -0 is code 0x80
+    assert list(e4m3_encode(np.array([-1e-30, -0.0, 0.0, 1e-30]))) == [0x80, 0x80, 0x00, 0x00]
 
 
 @pytest.mark.parametrize("N,d", [(64, 8), (130, 16), (1, 4)])
