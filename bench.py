@@ -229,6 +229,47 @@ def time_configs(torch, min_warmup_s):
                           "visible_fraction": visible / (B * H * N * N), "avg_us": us, "tflops": tflops,
                           "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "source_digest": source_digest()}), flush=True)
 
+    # FP8 forward (e4m3 Q, K with per-64-row scales, bf16 V) and the block-wise quantiser (HBM-bound)
+    def timed(run, reps=20):
+        t0 = time.perf_counter()
+        n = 0
+        while n < 10 or time.perf_counter() - t0 < min(min_warmup_s, 0.5):
+            run()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(reps):
+            run()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        return hip.ms(e0, e1) / reps * 1e3
+
+    for B, H, N, d, causal in ((2, 16, 4096, 128, True), (2, 16, 4096, 128, False), (2, 16, 4096, 256, True)):
+        w = Workload(f"fwd_fp8_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9)
+        inp = make_workload_inputs(w)
+        dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+               for n in ("q", "k", "v")}
+        qc, qs = fa.quantize_fp8(dev["q"])
+        kc, ks = fa.quantize_fp8(dev["k"])
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        us = timed(lambda: fa.fwd_fp8(qc, qs, kc, ks, dev["v"], causal=causal, out=o, lse=lse))
+        f_fwd, _ = flops(B, H, N, d, causal)
+        tflops = f_fwd / (us * 1e-6) / 1e12
+        print(json.dumps({"workload": w.name, "entry": "fa_fwd_fp8", "avg_us": us, "tflops": tflops,
+                          "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "peak_note": "fraction of the bf16 peak",
+                          "source_digest": source_digest()}), flush=True)
+        if causal and d == 128:
+            us_q = timed(lambda: fa.quantize_fp8(dev["q"], codes=qc, scale=qs))
+            qbytes = B * H * N * d * 3 + B * H * (-(-N // 64)) * 4  # read bf16, write codes and scales
+            print(json.dumps({"workload": f"quantize_fp8_b{B}h{H}n{N}d{d}", "entry": "fa_quantize_fp8",
+                              "avg_us": us_q, "gbs": qbytes / (us_q * 1e-6) / 1e9, "tflops": 0.0,
+                              "frac_of_peak": qbytes / (us_q * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                              "peak_note": "fraction of HBM bandwidth", "source_digest": source_digest()}), flush=True)
+
     # backward at head dim 256 (the backward at d = 128 is the headline line): both kernels timed on their own
     for B, H, N, d, causal in ((2, 16, 4096, 256, True),):
         w = Workload(f"bwd_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal, seed=9,
@@ -375,8 +416,8 @@ def main():
                     help="only run a plain device copy of known size (for scaling the HBM byte counters)")
     ap.add_argument("--configs", action="store_true",
                     help="only time the forward on every forward workload of fa_inputs.WORKLOADS, on head dim "
-                         "256, split-KV and block-sparse shapes, and the backward at head dim 256 (one JSON line "
-                         "each; not the headline line)")
+                         "256, split-KV, block-sparse and FP8 shapes, the FP8 quantiser, and the backward at head "
+                         "dim 256 (one JSON line each; not the headline line)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs "
                          "of a short bench run and of a --copy-calibration run (no GPU needed)")

@@ -119,6 +119,37 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
                        int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                        hipStream_t stream);
 
+/* FP8 inputs: e4m3 codes (OCP 8-bit float: 1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; largest value 448) with one float32 scale per
+ * FA_FP8_BLOCK consecutive rows of a head, x ~= value(code) * scale. */
+#define FA_FP8_BLOCK 64
+
+/* Block-wise quantisation of a bf16 tensor x [B, H, N, d] (d = 64, 128 or
+ * 256) for fa_fwd_fp8: per block of FA_FP8_BLOCK rows of one (b, h),
+ * scale = max|block| / 448 (1 for a block of zeros) and code = e4m3(x / scale),
+ * both float32 divisions correctly rounded, codes rounded to nearest even
+ * (the block scale factors of "Flash Attention V3技术解析" (mlqm.cn), section
+ * 3.2, with the largest e4m3 value as the divisor). codes: device uint8
+ * [B, H, N, d]; scale: device float32 [B, H, ceil(N / FA_FP8_BLOCK)]. Same
+ * pointer, alignment and error rules as fa_fwd. */
+int fa_quantize_fp8(const void* x, unsigned char* codes, float* scale, int B, int H, int N, int d,
+                    hipStream_t stream);
+
+/* Forward attention with FP8 queries and keys (mixed precision: the Q K^T
+ * product runs on the FP8 matrix unit, as the FP8 variant of "Flash Attention
+ * V3技术解析" (mlqm.cn), sections 1.3 and 3.2, does with block-wise scales; the
+ * softmax, P and V stay float32 / bf16, where "4.3 FlashAttention-2与
+ * FlashAttention-3演进" (aiknowledge.cn), FlashAttention-3 section 2, keeps
+ * BF16). q_codes [B, Hq, N, d] and k_codes [B, Hkv, N, d] are e4m3 codes with
+ * scales q_scale [B, Hq, ceil(N / 64)] and k_scale [B, Hkv, ceil(N / 64)]
+ * (as written by fa_quantize_fp8); v is bf16 [B, Hkv, N, d]; o bf16, lse
+ * float32 as in fa_fwd. The result is attention on the dequantised Q and K.
+ * d = 128 or 256 (FA_ERR_UNSUPPORTED otherwise); other rules as fa_fwd. */
+int fa_fwd_fp8(const unsigned char* q_codes, const unsigned char* k_codes, const void* v,
+               const float* q_scale, const float* k_scale, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (0 on invalid sizes). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

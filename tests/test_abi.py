@@ -26,8 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd",
-                                    "fa_fwd_blocksparse", "fa_fwd_f32", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
+                                    "fa_fwd_blocksparse", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_bytes", "fa_quantize_fp8", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -146,6 +146,37 @@ def test_blocksparse_argument_errors():
     assert call(ptrs=[BAD, BAD, BAD, NULL, BAD]) == INV
     assert call(d=256, ptrs=[NULL] * 5) == INV
     assert call(B=0, ptrs=[NULL] * 5, mask=NULL) == FA_OK
+
+
+def test_fp8_argument_errors():
+    from tiled_online_softmax_fa_amd import FA_ERR_INVALID_ARG as INV, FA_ERR_UNSUPPORTED as UNS, FA_OK
+
+    lib = _lib()
+
+    def fwd(ptrs=None, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, N=8, d=128, causal=0, scale=0.125)
+        a.update(kw)
+        p = ptrs or [BAD] * 7
+        return lib.fa_fwd_fp8(*p, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], NULL)
+
+    assert fwd(d=64) == UNS
+    assert fwd(d=96) == UNS
+    assert fwd(Hq=3, Hkv=2) == INV
+    assert fwd(ptrs=[BAD, BAD, BAD, NULL, BAD, BAD, BAD]) == INV  # q_scale
+    assert fwd(ptrs=[NULL] + [BAD] * 6) == INV
+    assert fwd(scale=0.0) == INV
+    assert fwd(B=0, ptrs=[NULL] * 7) == FA_OK
+
+    def quant(ptrs=None, **kw):
+        a = dict(B=1, H=2, N=8, d=128)
+        a.update(kw)
+        p = ptrs or [BAD] * 3
+        return lib.fa_quantize_fp8(*p, a["B"], a["H"], a["N"], a["d"], NULL)
+
+    assert quant(d=96) == UNS
+    assert quant(N=-1) == INV
+    assert quant(ptrs=[BAD, NULL, BAD]) == INV
+    assert quant(N=0, ptrs=[NULL] * 3) == FA_OK
 
 
 def test_status_strings():

@@ -78,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     ll = ctypes.c_longlong
     lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, ll, ll, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_blocksparse.restype = i
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.fa_quantize_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -193,6 +197,60 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, out=None, lse=None,
     st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), int(n_splits), _stream_ptr(q))
     _check(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+FP8_BLOCK = 64  # FA_FP8_BLOCK
+
+
+def quantize_fp8(x, codes=None, scale=None):
+    """Block-wise e4m3 quantisation of a bf16 tensor [B, H, N, d]: returns (codes uint8 [B, H, N, d],
+    scale float32 [B, H, ceil(N / 64)]) with x ~= e4m3(codes) * scale."""
+    torch = _torch()
+    _require(x, torch.bfloat16, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    nb = -(-N // FP8_BLOCK)
+    if codes is None:
+        codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    _require(codes, torch.uint8, "codes")
+    _require(scale, torch.float32, "scale")
+    if tuple(codes.shape) != (B, H, N, d) or tuple(scale.shape) != (B, H, nb):
+        raise ValueError("codes/scale have the wrong shape")
+    st = load_library().fa_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scale), B, H, N, d, _stream_ptr(x))
+    _check(st, "fa_quantize_fp8")
+    return codes, scale
+
+
+def fwd_fp8(q_codes, q_scale, k_codes, k_scale, v, causal=False, scale=None, out=None, lse=None):
+    """Forward attention with e4m3 q, k (codes uint8 and per-64-row float32 scales, as from quantize_fp8)
+    and bf16 v. Returns (o bf16, lse float32)."""
+    torch = _torch()
+    _require(q_codes, torch.uint8, "q_codes")
+    _require(k_codes, torch.uint8, "k_codes")
+    _require(v, torch.bfloat16, "v")
+    _require(q_scale, torch.float32, "q_scale")
+    _require(k_scale, torch.float32, "k_scale")
+    B, Hq, Hkv, N, d = _dims(q_codes, k_codes, v)
+    nb = -(-N // FP8_BLOCK)
+    if tuple(q_scale.shape) != (B, Hq, nb) or tuple(k_scale.shape) != (B, Hkv, nb):
+        raise ValueError(f"q_scale/k_scale must be [B, H, {nb}]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=v.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=v.device)
+    _require(out, torch.bfloat16, "out")
+    _require(lse, torch.float32, "lse")
+    if tuple(out.shape) != (B, Hq, N, d) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    st = load_library().fa_fwd_fp8(_ptr(q_codes), _ptr(k_codes), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(out),
+                                   _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_ptr(v))
+    _check(st, "fa_fwd_fp8")
     return out, lse
 
 

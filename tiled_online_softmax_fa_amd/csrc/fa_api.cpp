@@ -184,6 +184,47 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
   return launch_status(fa::launch_fwd_bf16_blocksparse(p, d, causal != 0, stream));
 }
 
+int fa_quantize_fp8(const void* x, unsigned char* codes, float* scale, int B, int H, int N, int d,
+                    hipStream_t stream) {
+  static_assert(FA_FP8_BLOCK == fa::kFp8Block, "FP8 block");
+  int st = check_shapes(B, H, H, N, d, 0, 1.0f, true);
+  if (st != FA_OK) return st;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({x, codes, scale});
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  return launch_status(fa::launch_quantize_fp8(x, codes, scale, B * H, N, d, stream));
+}
+
+int fa_fwd_fp8(const unsigned char* q_codes, const unsigned char* k_codes, const void* v, const float* q_scale,
+               const float* k_scale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream) {
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
+  if (st != FA_OK) return st;
+  if (d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q_codes, k_codes, v, o, lse});
+  if (st != FA_OK) return st;
+  if (q_scale == nullptr || k_scale == nullptr) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdParams p{};
+  p.q = q_codes;
+  p.k = k_codes;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.scale_log2 = scale * kLog2e;
+  p.q_descale = q_scale;
+  p.k_descale = k_scale;
+  return launch_status(fa::launch_fwd_fp8(p, d, causal != 0, stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
   return bwd_workspace(B, Hq, N, d);

@@ -28,6 +28,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define FA_LDS __attribute__((address_space(3)))
 #define FA_GLOBAL __attribute__((address_space(1)))
@@ -42,6 +43,15 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 }
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands e4m3 and unit block
+// scales (E8M0 127 = 2^0): D[16x16] = A[16x128] * B[128x16] + C. Each lane
+// supplies 32 bytes: A lane l row (l % 16), B lane l column (l % 16), with the
+// same k positions for byte e of lane l in A and in B, so operands loaded with
+// one common byte order per lane contract over matching k. C/D as above.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // 2^x on the transcendental unit (v_exp_f32): 2^-inf = 0.

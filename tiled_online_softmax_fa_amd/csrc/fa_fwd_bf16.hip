@@ -100,13 +100,21 @@ struct KVSwizzle {
 // as the causal skip streams only the tiles below the diagonal. A wave
 // whose own query block does not see a listed block masks it out element
 // by element. Rows that see no key get O = 0 and lse = -inf.
+// F8: q and k hold e4m3 codes with one fp32 scale per 64 rows (block-wise
+// quantisation of the inputs of Q K^T, "Flash Attention V3技术解析" (mlqm.cn)
+// sections 1.3 and 3.2); S^T = K Q^T runs on the FP8 matrix instruction
+// (16x16x128, the whole head dim of a 16 x 16 block in one or two steps),
+// and the block scales fold into the per-chunk exponent factor. V, P, the
+// softmax and O are as in the bf16 path (BF16 where precision matters, as in
+// "4.3 FlashAttention-2与FlashAttention-3演进", FlashAttention-3 section 2).
 template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false, int BN = 64,
-          bool SPARSE = false>
+          bool SPARSE = false, bool F8 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
 void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = QPW * NW;
   static_assert(BN == 32 || BN == 64, "one or two 32-key chunks per tile");
-  constexpr int OPS = 2 * (BN * D * 2 / 1024) / NW;  // copy instructions per wave per tile (K and V)
+  // copy instructions per wave per tile (K and V[, the K scale])
+  constexpr int OPS = F8 ? (BN * D / 1024) / NW + (BN * D * 2 / 1024) / NW + 1 : 2 * (BN * D * 2 / 1024) / NW;
   static_assert(STAGES >= 3, "the copy of tile t+STAGES-1 is issued while tile t is read");
   constexpr int QB = QPW / 16;           // 16-query blocks per wave
   constexpr int DC = D / 32;             // k-steps of S^T = K Q^T
@@ -119,12 +127,24 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int CH = 2 * D / 16;
   using Swz = KVSwizzle<D>;
   static_assert(COPIES % NW == 0, "K/V copy must split evenly over the waves");
+  // stage = K tile (bf16 rows, or e4m3 rows of D bytes), V tile, and (F8) the tile's K scale
+  constexpr int KROW = F8 ? D : 2 * D;
+  constexpr int K_TILE_BYTES = BN * KROW;
+  constexpr int V_OFF = K_TILE_BYTES;
+  constexpr int SCALE_OFF = K_TILE_BYTES + TILE_BYTES;
+  constexpr int STAGE_BYTES = SCALE_OFF + (F8 ? 256 : 0);
+  constexpr int DC8 = D / 128;                                  // F8: 128-byte k-steps of S^T
+  constexpr int K8_COPIES_PER_WAVE = K_TILE_BYTES / 1024 / NW;  // F8 copies of K per wave
+  constexpr int K8_ROWS = 1024 / KROW, K8_CH = KROW / 16;
+  using Swz8 = KVSwizzle<D / 2>;                                // F8 K rows: D bytes
+  static_assert(!F8 || ((D == 128 || D == 256) && !SPARSE && !SPLIT && K_TILE_BYTES % (1024 * NW) == 0),
+                "FP8: head dim 128 or 256, plain forward");
   constexpr int SB = kSparseBlock;  // block-mask block (queries and keys)
   constexpr int TPB = SB / BN;      // key tiles per mask block
   static_assert(!SPARSE || (BM % SB == 0 && BM / SB <= 2 && !SPLIT), "sparse: 1 or 2 query blocks per workgroup");
 
-  // ring of STAGES x (K tile, V tile)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * 2 * TILE_BYTES];
+  // ring of STAGES x (K tile, V tile[, K scale])
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[STAGES * STAGE_BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
   // sparse: listed key blocks, bits 0-13 block index, bit 14 + i: query block i of the workgroup sees it
   __shared__ uint16_t blk_list[SPARSE ? kSparseMaxBlocks : 1];
@@ -209,7 +229,33 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // ---- K/V tile copies (asynchronous; published by the barrier of the tile)
   auto issue_tile_copy = [&](int t) __attribute__((always_inline)) {
     const int kv0 = kv_tile_of(t) * BN;
-    const uint32_t kdst = lds_address(smem) + ((t - t_lo) % STAGES) * 2 * TILE_BYTES;
+    const uint32_t kdst = lds_address(smem) + ((t - t_lo) % STAGES) * STAGE_BYTES;
+    if constexpr (F8) {
+      const unsigned char* k8 = (const unsigned char*)p.k + ((size_t)(b * p.Hkv + hk) * N) * D;
+#pragma unroll
+      for (int c = 0; c < K8_COPIES_PER_WAVE; ++c) {
+        const int piece = wave * K8_COPIES_PER_WAVE + c;
+        const int prow = piece * K8_ROWS + lane / K8_CH;
+        const int pch = lane % K8_CH;
+        const int grow = min(kv0 + prow, N - 1);
+        copy16_global_to_lds_async(k8, (uint32_t)(grow * D + (pch ^ Swz8::k_swz(prow)) * 16), kdst + piece * 1024);
+      }
+#pragma unroll
+      for (int c = 0; c < COPIES_PER_WAVE; ++c) {
+        const int piece = wave * COPIES_PER_WAVE + c;
+        const int prow = piece * ROWS_PER_COPY + lane / CH;
+        const int pch = lane % CH;
+        const int grow = min(kv0 + prow, N - 1);
+        const int vch = (((pch >> 1) ^ Swz::v_swz(prow)) << 1) | (pch & 1);
+        copy16_global_to_lds_async(vg, (uint32_t)(grow * D + vch * 8) * 2, kdst + V_OFF + piece * 1024);
+      }
+      // the tile's K scale (every wave copies it, so all waves count the same copies)
+      if (lane == 0) {
+        const float* ks = p.k_descale + (size_t)(b * p.Hkv + hk) * ((N + kFp8Block - 1) / kFp8Block);
+        copy4_global_to_lds_async(ks, (uint32_t)(kv0 / kFp8Block) * 4, kdst + SCALE_OFF);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < COPIES_PER_WAVE; ++c) {
       const int piece = wave * COPIES_PER_WAVE + c;
@@ -226,13 +272,28 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   for (int t = t_lo; t < t_lo + STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
 
   // Q^T fragments (B operand of S^T = K Q^T), held for the whole key loop.
-  bf16x8 qf[QB][DC];
+  bf16x8 qf[F8 ? 1 : QB][F8 ? 1 : DC];
+  i32x8 qf8[F8 ? QB : 1][F8 ? DC8 : 1];  // F8: bytes 32 g .. 32 g + 31 of each 128-byte k-step
+  if constexpr (F8) {
+    const unsigned char* q8 = (const unsigned char*)p.q + ((size_t)(b * p.Hq + h) * N) * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = min(qw0 + qb * 16 + L, N - 1);
-    const u32x4* src = (const u32x4*)(qg + (size_t)row * D + g * 8);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = min(qw0 + qb * 16 + L, N - 1);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[qb][dc] = __builtin_bit_cast(bf16x8, src[dc * 4]);
+      for (int dc = 0; dc < DC8; ++dc) {
+        const u32x4* src = (const u32x4*)(q8 + (size_t)row * D + dc * 128 + g * 32);
+        const u32x4 lo = src[0], hi = src[1];
+        qf8[qb][dc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = min(qw0 + qb * 16 + L, N - 1);
+      const u32x4* src = (const u32x4*)(qg + (size_t)row * D + g * 8);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) qf[qb][dc] = __builtin_bit_cast(bf16x8, src[dc * 4]);
+    }
   }
 
   f32x4 acc[DB][QB];
@@ -247,13 +308,28 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     l_part[qb] = 0.f;
   }
   const float c = p.scale_log2;
+  // exponent factor of the scores in s_cur (F8: times the Q and K block scales)
+  float c_s = c;
+  float c_q = c;  // F8: c times this wave's Q block scale (its rows lie in one 64-row block)
+  if constexpr (F8) {
+    const int n_qblk = (N + kFp8Block - 1) / kFp8Block;
+    c_q = c * p.q_descale[(size_t)(b * p.Hq + h) * n_qblk + min(qw0, N - 1) / kFp8Block];
+  }
 
   // Lane parts of the LDS fragment addresses (the stage and chunk parts are
   // compile-time constants at every use, so they fold into the instruction
   // offsets and no address arithmetic runs per chunk).
-  int k_off[DC];  // K row L of a 16-key block, 16-byte chunk dc*4 + g (swizzled)
+  int k_off[F8 ? 1 : DC];  // K row L of a 16-key block, 16-byte chunk dc*4 + g (swizzled)
+  int k8_off[F8 ? DC8 : 1][2];  // F8: K row L, 16-byte chunks 8 dc + 2 g and 8 dc + 2 g + 1 (swizzled)
+  if constexpr (F8) {
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) k_off[dc] = L * (2 * D) + (((dc * 4 + g) ^ Swz::k_swz(L)) * 16);
+    for (int dc = 0; dc < DC8; ++dc)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) k8_off[dc][hh] = L * KROW + (((dc * 8 + 2 * g + hh) ^ Swz8::k_swz(L)) * 16);
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) k_off[dc] = L * (2 * D) + (((dc * 4 + g) ^ Swz::k_swz(L)) * 16);
+  }
   int v_off[DB];  // V row 4g + L/4 of a 32-key chunk, 32-byte chunk db (swizzled), 8 bytes at 8 (L & 3)
   {
     const int vrow = 4 * g + (L >> 2);
@@ -271,8 +347,20 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   };
   // V^T fragments (A operand of O^T += V^T P^T): rows d = 16 db + lane % 16,
   // element e < 4 -> key 4g + e, e >= 4 -> key 16 + 4g + e - 4 of the chunk
+  // F8: K fragments of chunk cc, 32 bytes per lane per 128-byte k-step
+  auto read_k8 = [&](const lds_u8* kt, int cc, i32x8 (&kf)[2][DC8 > 0 ? DC8 : 1]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int dc = 0; dc < DC8; ++dc) {
+        const lds_u8* rowp = kt + (cc * 32 + hb * 16) * KROW;
+        const u32x4 lo = *(const FA_LDS u32x4*)(rowp + k8_off[dc][0]);
+        const u32x4 hi = *(const FA_LDS u32x4*)(rowp + k8_off[dc][1]);
+        kf[hb][dc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+  };
   auto read_v = [&](const lds_u8* kt, int cc, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
-    const lds_u8* vt = kt + TILE_BYTES + cc * 32 * (2 * D);
+    const lds_u8* vt = kt + V_OFF + cc * 32 * (2 * D);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const i16x4 lo = lds_read_tr16_b64(vt + v_off[db]);
@@ -314,7 +402,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
       mx = fmaxf(fmaxf(mx, s[0][qb][3]), s[1][qb][0]);
       mx = fmaxf(fmaxf(mx, s[1][qb][1]), s[1][qb][2]);
-      tmax[qb] = fmaxf(mx, s[1][qb][3]) * c;
+      tmax[qb] = fmaxf(mx, s[1][qb][3]) * c_s;
     }
   };
   // move the reference maximum if some score exceeds it by more than the slack
@@ -346,8 +434,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       float e[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        e[r] = exp2_fast(fmaf(s[0][qb][r], c, neg_m));
-        e[4 + r] = exp2_fast(fmaf(s[1][qb][r], c, neg_m));
+        e[r] = exp2_fast(fmaf(s[0][qb][r], c_s, neg_m));
+        e[4 + r] = exp2_fast(fmaf(s[1][qb][r], c_s, neg_m));
       }
       u32x4 packed = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                       pack_bf16x2(e[6], e[7])};
@@ -369,9 +457,25 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
   // S^T of chunk ch (K tile at kt, position cc), masked when MASK, and the reference update.
   auto scores = [&](const lds_u8* kt, int cc, int ch, auto mask, bool sees = true) __attribute__((always_inline)) {
-    bf16x8 kf[2][DC];
-    read_k(kt, cc, kf);
-    compute_s(kf, s_cur);
+    if constexpr (F8) {
+      i32x8 kf[2][DC8 > 0 ? DC8 : 1];
+      read_k8(kt, cc, kf);
+      if (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s_cur[hb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC8; ++dc) s_cur[hb][qb] = mfma_fp8_16x16x128(kf[hb][dc], qf8[qb][dc], s_cur[hb][qb]);
+        }
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
+      c_s = c_q * *(const FA_LDS float*)(kt + SCALE_OFF);
+    } else {
+      bf16x8 kf[2][DC];
+      read_k(kt, cc, kf);
+      compute_s(kf, s_cur);
+    }
     if (decltype(mask)::value) apply_mask(ch, s_cur, sees);
     float tmax[QB];
     chunk_max(s_cur, tmax);
@@ -430,7 +534,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // run in a loop of their own with branch-free bodies; the diagonal and the
   // end of the sequence take the masked path. Stage bases are run-time values.
   auto stage_base = [&](int t) __attribute__((always_inline)) {
-    return smem + uniform(((t - t_lo) % STAGES) * 2 * TILE_BYTES);
+    return smem + uniform(((t - t_lo) % STAGES) * STAGE_BYTES);
   };
   auto publish_next = [&](int t) __attribute__((always_inline)) {
     if (t + STAGES - 2 < n_kv) {
@@ -660,6 +764,23 @@ hipError_t launch_fwd_bf16_blocksparse(const FwdParams& p, int d, bool causal, h
   if (d == 256) return causal ? launch_fwd_bf16_sparse_cfg<256, true>(p, stream) : launch_fwd_bf16_sparse_cfg<256, false>(p, stream);
   if (d == 128) return causal ? launch_fwd_bf16_sparse_cfg<128, true>(p, stream) : launch_fwd_bf16_sparse_cfg<128, false>(p, stream);
   if (d == 64) return causal ? launch_fwd_bf16_sparse_cfg<64, true>(p, stream) : launch_fwd_bf16_sparse_cfg<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_fp8_cfg(const FwdParams& p_in, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  FwdParams p = p_in;
+  p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
+  const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, C::QPW, C::NW, true, C::STAGES, false, C::BN, false, true>),
+                     dim3(grid), dim3(C::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 256) return causal ? launch_fwd_fp8_cfg<256, true>(p, stream) : launch_fwd_fp8_cfg<256, false>(p, stream);
+  if (d == 128) return causal ? launch_fwd_fp8_cfg<128, true>(p, stream) : launch_fwd_fp8_cfg<128, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -25,6 +25,10 @@ struct FwdParams {
   // block_mask[b * mask_stride_b + h * mask_stride_h + qb * n_blk + kb]
   const unsigned char* block_mask;
   long long mask_stride_b, mask_stride_h;
+  // FP8 only: q and k hold e4m3 codes; one fp32 scale per 64 rows of a head,
+  // q_descale [B][Hq][n_qblk], k_descale [B][Hkv][n_qblk], n_qblk = ceil(N / 64)
+  const float* q_descale;
+  const float* k_descale;
 };
 
 struct BwdParams {
@@ -53,6 +57,12 @@ constexpr int kSparseBlock = 128;
 constexpr int kSparseMaxBlocks = 1024;
 constexpr int kSparseMaxN = kSparseBlock * kSparseMaxBlocks;
 hipError_t launch_fwd_bf16_blocksparse(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// FP8 forward (p.q, p.k e4m3 codes with p.q_descale / p.k_descale; d = 128 or 256)
+constexpr int kFp8Block = 64;
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
+// block-wise e4m3 quantisation of a bf16 [heads][N][d] tensor (d = 64, 128 or 256)
+hipError_t launch_quantize_fp8(const void* x, unsigned char* codes, float* scale, int heads, int N, int d,
+                               hipStream_t stream);
 // events: NULL or 3 events recorded before/between/after the two backward kernels
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* events);
 
