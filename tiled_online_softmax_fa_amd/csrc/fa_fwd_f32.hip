@@ -6,16 +6,24 @@
 // S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x4_f32.
 //
 // This path serves short, latency-bound problems (its measured case is one
-// head of 256 keys), so it favours simplicity: 4 waves x 16 query rows per
-// workgroup (the 64-row query block of the mhpq.cn page, section 3.1),
-// 32-key K/V tiles staged through two LDS buffers (each tile's global loads
-// are issued one tile ahead, into registers), and rows padded to d + 4
-// floats so the fragment reads of 16 consecutive rows fall in different
-// banks (the row padding of mhpq.cn section 5.2).
+// head of 256 keys), where a query-parallel grid alone leaves each wave a
+// long chain of dependent key tiles. So the keys are split too: one
+// workgroup of 8 waves per 16-row query block, wave w takes key tiles w,
+// w + 8, w + 16, ... (16 keys each) with its own running max, sum and
+// accumulator, and the 8 partial results are merged at the end with the
+// online-softmax rule one level up (the merge of partial results over key
+// ranges, "FlashAttention技术解析" section 4.2):
+//   M = max_w m_w,  O = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w.
+// Each wave loads its K and V tiles from global memory straight into the
+// operand registers of the matrix instruction, one tile ahead, so the key
+// loop needs no LDS and no barrier; LDS is used once, for the merge.
 //
-// The P^T accumulator registers feed O^T += V^T P^T directly: for the r-th
-// 4-key step of a 16-key block, lane l's register r holds key 4(l/16) + r,
-// which is exactly the k-slot l/16 the instruction reads from lane l.
+// Operand layouts (fragment layouts in fa_common.hpp): for S^T the lane with
+// query column L and k-slot g takes head-dim entries g * D/4 .. g * D/4 +
+// D/4 - 1, one per k-step, for both K and Q (any common order of the head
+// dim contracts correctly); for O^T += V^T P^T, at the r-th 4-key step lane
+// (L, g) holds P^T of key 4g + r, which is the instruction's k-slot g, so
+// it supplies V[4g + r][16 db + L] as the A operand.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -24,15 +32,16 @@ namespace fa {
 constexpr float kRescaleSlackF32 = 8.0f;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
-  constexpr int QPW = 16, NW = 4, BM = QPW * NW, BN = 32;
-  constexpr int KB = BN / 16;
-  constexpr int DS = D / 4;   // k-steps of S^T
-  constexpr int DB = D / 16;  // 16-row blocks of O^T
-  constexpr int LD = D + 4;   // padded LDS row (floats)
-  // two K/V tile buffers: tile t+1 is written while tile t is read
-  __shared__ __attribute__((aligned(16))) float ks2[2][BN * LD];
-  __shared__ __attribute__((aligned(16))) float vs2[2][BN * LD];
+__global__ __launch_bounds__(512, 1) void fa_fwd_f32_kernel(FwdParams p) {
+  constexpr int NW = 8;      // waves per workgroup = key-range parts of one query block
+  constexpr int BM = 16;     // query rows per workgroup
+  constexpr int BN = 16;     // keys per tile
+  constexpr int DS = D / 4;  // k-steps of S^T
+  constexpr int DB = D / 16; // 16-row blocks of O^T
+  constexpr int LDO = D + 4; // padded merge row (floats)
+  __shared__ float sm_m[NW][BM];
+  __shared__ float sm_l[NW][BM];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][BM * LDO];
 
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -51,16 +60,45 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
   float* __restrict__ lseg = p.lse + (size_t)(b * p.Hq + h) * N;
 
   const int q0 = tc.tile * BM;
-  const int qw0 = q0 + wave * QPW;
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_kv = (kv_end + BN - 1) / BN;
-  const int n_kv_wave = (qw0 < N) ? ((CAUSAL ? min(N, qw0 + QPW) : N) + BN - 1) / BN : 0;
+  const int n_kv = (kv_end + BN - 1) / BN;  // key tiles with a visible key for the block
+
+  // K and V operands of one tile, and the loads that fill them
+  struct Tile {
+    float k[DS];
+    float v[4][DB];
+  };
+  auto load_tile = [&](int t, Tile& x) __attribute__((always_inline)) {
+    const int krow = min(t * BN + L, N - 1);  // rows past the end: any valid row, masked below
+    const f32x4* ks = (const f32x4*)(kg + (size_t)krow * D + g * DS);
+#pragma unroll
+    for (int j = 0; j < DS / 4; ++j) {
+      const f32x4 v4 = ks[j];
+      x.k[4 * j] = v4[0];
+      x.k[4 * j + 1] = v4[1];
+      x.k[4 * j + 2] = v4[2];
+      x.k[4 * j + 3] = v4[3];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int vrow = min(t * BN + 4 * g + r, N - 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) x.v[r][db] = vg[(size_t)vrow * D + db * 16 + L];
+    }
+  };
 
   float qf[DS];
   {
-    const int row = min(qw0 + L, N - 1);
+    const int row = min(q0 + L, N - 1);
+    const f32x4* qs = (const f32x4*)(qg + (size_t)row * D + g * DS);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[ds] = qg[(size_t)row * D + ds * 4 + g];
+    for (int j = 0; j < DS / 4; ++j) {
+      const f32x4 v4 = qs[j];
+      qf[4 * j] = v4[0];
+      qf[4 * j + 1] = v4[1];
+      qf[4 * j + 2] = v4[2];
+      qf[4 * j + 3] = v4[3];
+    }
   }
   f32x4 acc[DB];
 #pragma unroll
@@ -68,66 +106,23 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
   float m_ref = kNegInf, l_part = 0.f;
   const float c = p.scale_log2;
 
-  // Tile loads go global -> registers one tile ahead (their latency overlaps
-  // the math of the current tile), then registers -> LDS at the top of the
-  // next iteration; one barrier per tile publishes the tile and, with two
-  // buffers, also guarantees the buffer written next is no longer read.
-  constexpr int VEC = BN * D / 4;             // float4 pieces per tensor
-  constexpr int PER = VEC / (NW * 64);        // pieces per thread
-  static_assert(VEC % (NW * 64) == 0, "tile split");
-  f32x4 kreg[PER], vreg[PER];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = tid + j * NW * 64;
-      const int row = i / (D / 4), c4 = i % (D / 4);
-      const int grow = min(t * BN + row, N - 1);
-      kreg[j] = *(const f32x4*)(kg + (size_t)grow * D + c4 * 4);
-      vreg[j] = *(const f32x4*)(vg + (size_t)grow * D + c4 * 4);
-    }
-  };
-  if (n_kv > 0) load_tile(0);
-  for (int t = 0; t < n_kv; ++t) {
+  Tile cur, nxt;
+  if (wave < n_kv) load_tile(wave, cur);
+  for (int t = wave; t < n_kv; t += NW) {
+    if (t + NW < n_kv) load_tile(t + NW, nxt);
     const int kv0 = t * BN;
-    float* ks = ks2[t & 1];
-    float* vs = vs2[t & 1];
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = tid + j * NW * 64;
-      const int row = i / (D / 4), c4 = i % (D / 4);
-      *(f32x4*)(ks + row * LD + c4 * 4) = kreg[j];
-      *(f32x4*)(vs + row * LD + c4 * 4) = vreg[j];
+    for (int ds = 0; ds < DS; ++ds) s = mfma_f32_16x16x4(cur.k[ds], qf[ds], s);
+    if ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kv0 + 4 * g + r;
+        const bool visible = key < N && (!CAUSAL || key <= q0 + L);
+        s[r] = visible ? s[r] : kNegInf;
+      }
     }
-    if (t + 1 < n_kv) load_tile(t + 1);
-    __syncthreads();
-    if (t >= n_kv_wave) continue;
-
-    f32x4 s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-      const float* krow = ks + (kb * 16 + L) * LD + g;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) a = mfma_f32_16x16x4(krow[ds * 4], qf[ds], a);
-      s[kb] = a;
-    }
-    const bool need_mask = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qw0);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kv0 + kb * 16 + g * 4 + r;
-          const bool visible = key < N && (!CAUSAL || key <= qw0 + L);
-          s[kb][r] = visible ? s[kb][r] : kNegInf;
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float tmax = mx * c;
+    const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * c;
     if (wave_any(tmax > m_ref + kRescaleSlackF32)) {
       const float m_new = fmaxf(m_ref, max_over_row_groups(tmax));
       const float alpha = (m_ref == kNegInf) ? 0.f : exp2_fast(m_ref - m_new);
@@ -136,39 +131,57 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_f32_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
-    const float neg_m = -m_ref;
+    // a row that has seen only masked keys keeps m = -inf; its exponentials are 2^-inf = 0
+    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int r = 0; r < 4; ++r) {
+      s[r] = exp2_fast(fmaf(s[r], c, neg_m));
+      l_part += s[r];
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[kb][r] = exp2_fast(fmaf(s[kb][r], c, neg_m));
-        l_part += s[kb][r];
-      }
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[db] = mfma_f32_16x16x4(vs[(kb * 16 + 4 * g + r) * LD + db * 16 + L], s[kb][r], acc[db]);
+      for (int db = 0; db < DB; ++db) acc[db] = mfma_f32_16x16x4(cur.v[r][db], s[r], acc[db]);
+    cur = nxt;
   }
 
-  const float l = sum_over_row_groups(l_part);
-  const int row = qw0 + L;
-  if (row < N) {
-    const float inv = 1.0f / l;
+  // ---- merge the NW partial results of each query row
+  const float l_w = sum_over_row_groups(l_part);
+  if (g == 0) {
+    sm_m[wave][L] = m_ref;
+    sm_l[wave][L] = l_w;
+  }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *(f32x4*)(og + (size_t)row * D + db * 16 + g * 4) = acc[db] * inv;
-    if (g == 0) lseg[row] = (m_ref + log2_fast(l)) * kLn2;
+  for (int db = 0; db < DB; ++db) *(f32x4*)(&sm_o[wave][L * LDO + db * 16 + 4 * g]) = acc[db];
+  __syncthreads();
+  constexpr int C4 = D / 4;  // 4-column groups per row
+  for (int i = tid; i < BM * C4; i += NW * 64) {
+    const int r = i / C4, c4 = i - r * C4;
+    const int row = q0 + r;
+    if (row >= N) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][r];
+      const float wt = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);  // parts without keys weigh 0
+      lsum += wt * sm_l[w][r];
+      o += wt * *(const f32x4*)(&sm_o[w][r * LDO + c4 * 4]);
+    }
+    *(f32x4*)(og + (size_t)row * D + c4 * 4) = o * (1.0f / lsum);
+    if (c4 == 0) lseg[row] = (M + log2_fast(lsum)) * kLn2;
   }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_f32_cfg(const FwdParams& p_in, hipStream_t stream) {
   FwdParams p = p_in;
-  p.n_tiles = (p.N + 63) / 64;
+  p.n_tiles = (p.N + 15) / 16;
   const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
-  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
