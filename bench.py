@@ -67,26 +67,35 @@ def flops(B, H, N, d, causal):
     return fwd, 2.5 * fwd
 
 
-def source_digest():
+# the sources each timed kernel is compiled from (its own file and the shared headers)
+KERNEL_SOURCES = {
+    "fa_fwd_bf16_kernel": ("fa_fwd_bf16.hip", "fa_common.hpp", "fa_launch.hpp"),
+    "fa_bwd_dq_kernel": ("fa_bwd_bf16.hip", "fa_common.hpp", "fa_launch.hpp"),
+    "fa_bwd_dkdv_kernel": ("fa_bwd_bf16.hip", "fa_common.hpp", "fa_launch.hpp"),
+}
+
+
+def source_digest(names=None):
+    """sha256 (16 hex digits) of the named files under csrc/, or of all of them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_online_softmax_fa_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names if names is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key, launches_note):
-    """HBM bytes per launch from the committed PMC summary, if it is for the current sources."""
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the kernel's current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != source_digest():
-        return None
     k = t.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_key]):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 MFMA
@@ -358,7 +367,8 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
             continue
         rd = fetch[fk[0]] * 1024.0 * f_fetch
         wr = write[wk[0]] * 1024.0 * f_write
-        kernels[key] = {"hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr}
+        kernels[key] = {"hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                        "source_digest": source_digest(KERNEL_SOURCES[key])}
     out = {
         "source_digest": source_digest(),
         "workload": "causal attention fwd+bwd, B=2 H=16 N=4096 d=128 (bench.py default)",
