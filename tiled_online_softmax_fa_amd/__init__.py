@@ -6,8 +6,12 @@ passes raw pointers and the current stream through the C ABI declared in
 include/fa.h. There is no fallback: if libfa.so is missing or cannot be
 loaded, importing the ops raises.
 
-    o, lse = fwd(q, k, v, causal=True)              # bf16 [B,H,N,d]
-    o, lse = fwd_f32(q, k, v)                        # float32
+    o, lse = fwd(q, k, v, causal=True)              # bf16 [B,H,N,d], d = 64, 128, 256
+    o, lse = fwd_f32(q, k, v)                        # float32, d = 64, 128
+    o, lse = fwd_splitkv(q, k, v, 4, causal=True)    # keys of each query tile in 4 parts + merge
+    o, lse = fwd_blocksparse(q, k, v, mask)          # uint8/bool block mask, 128 x 128 blocks
+    qc, qs = quantize_fp8(q); kc, ks = quantize_fp8(k)
+    o, lse = fwd_fp8(qc, qs, kc, ks, v, causal=True) # e4m3 Q, K with per-64-row scales
     dq, dk, dv = bwd(q, k, v, o, lse, dout, causal=True)
     o = flash_attn(q, k, v, causal=True)             # autograd.Function
 """
@@ -25,6 +29,11 @@ __all__ = [
     "fwd_f32",
     "fwd_splitkv",
     "splitkv_workspace_bytes",
+    "fwd_blocksparse",
+    "SPARSE_BLOCK",
+    "quantize_fp8",
+    "fwd_fp8",
+    "FP8_BLOCK",
     "bwd",
     "bwd_workspace_bytes",
     "flash_attn",

@@ -12,8 +12,9 @@
 // work partitioning: each warp owns its own rows):
 //   * one workgroup of 8 waves per (query tile of 256 rows, batch * head), two
 //     waves per SIMD; each wave owns 32 consecutive query rows and never
-//     exchanges partial results with another wave;
-//   * K/V tiles of 64 keys are copied global -> LDS with 16-byte direct loads
+//     exchanges partial results with another wave (head dim 256: 128-row
+//     tiles, 16 rows per wave, so the accumulator keeps its register size);
+//   * K/V tiles of 64 keys (32 at head dim 256) are copied global -> LDS with 16-byte direct loads
 //     into a ring of STAGES stages. The copy of tile t+STAGES-1 is issued
 //     right after the single barrier that publishes tile t+1, so it overlaps
 //     the math of STAGES-2 tiles ("Flash Attention V3技术解析" section 2.1,
@@ -48,7 +49,7 @@
 // exponential is then at most 2^kRescaleSlack, and because acc and l share
 // the same reference the ratio acc / l, i.e. O, is the same number. The check
 // is one compare per row and a wave vote, so the per-chunk rescale of acc
-// (128 multiplies per lane) is skipped on almost every chunk.
+// (64 multiplies per lane at head dim 128) is skipped on almost every chunk.
 //
 // Causal (key j visible to query i iff j <= i): the key loop stops at the
 // last key tile holding a visible key for the workgroup's last query (tiles
@@ -56,6 +57,10 @@
 // section 2.1), each wave stops at its own diagonal, and the element mask is
 // applied only on chunks that straddle the diagonal or the end of the
 // sequence.
+//
+// The same kernel, through template flags described at its definition, also
+// runs split-KV (key-range parts of a query tile plus a merge kernel), a
+// block mask (block-sparse) and FP8 queries and keys.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -98,8 +103,9 @@ struct KVSwizzle {
 // query blocks sees (the union; causal drops blocks wholly above the
 // diagonal) into a list in LDS and then streams only those tiles, exactly
 // as the causal skip streams only the tiles below the diagonal. A wave
-// whose own query block does not see a listed block masks it out element
-// by element. Rows that see no key get O = 0 and lse = -inf.
+// skips the chunks of listed blocks that its own query block does not see
+// (and chunks above its diagonal or past the end). Rows that see no key get
+// O = 0 and lse = -inf.
 // F8: q and k hold e4m3 codes with one fp32 scale per 64 rows (block-wise
 // quantisation of the inputs of Q K^T, "Flash Attention V3技术解析" (mlqm.cn)
 // sections 1.3 and 3.2); S^T = K Q^T runs on the FP8 matrix instruction
