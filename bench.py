@@ -154,8 +154,8 @@ def time_configs(torch, min_warmup_s):
 
     for B, H, N, d, causal, split_list in ((2, 16, 4096, 128, False, (0,)),
                                           (2, 16, 4096, 256, True, (0,)), (2, 16, 4096, 256, False, (0,)),
-                                          (1, 8, 16384, 128, True, (0, 2, 4, 8)),
-                                          (1, 4, 8192, 128, False, (0, 2, 4, 8))):
+                                          (1, 8, 16384, 128, True, (0, 2, 4, 8, "auto")),
+                                          (1, 4, 8192, 128, False, (0, 2, 4, 8, "auto"))):
         w = Workload(f"{'splitkv_' if len(split_list) > 1 else 'fwd_'}b{B}h{H}n{N}d{d}{'_causal' if causal else ''}",
                      B, H, H, N, d, "bf16", causal, seed=9)
         inp = make_workload_inputs(w)
@@ -166,8 +166,9 @@ def time_configs(torch, min_warmup_s):
         f_fwd, _ = flops(B, H, N, d, causal)
         for splits in split_list:
             if splits:
-                ws = torch.empty(fa.splitkv_workspace_bytes(B, H, H, N, d, splits), dtype=torch.uint8, device="cuda:0")
-                run = lambda: fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], splits, causal=causal, out=o, lse=lse,
+                ns = 0 if splits == "auto" else splits
+                ws = torch.empty(fa.splitkv_workspace_bytes(B, H, H, N, d, ns), dtype=torch.uint8, device="cuda:0")
+                run = lambda: fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], ns, causal=causal, out=o, lse=lse,
                                              workspace=ws)
             else:
                 run = lambda: fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, out=o, lse=lse)

@@ -74,7 +74,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                hipStream_t stream);
 
 /* Bytes of device workspace fa_fwd_splitkv needs for these sizes and
- * n_splits (0 on invalid sizes or n_splits outside 1..64). */
+ * n_splits (0 on invalid sizes or n_splits outside 0..64; 0 = the automatic
+ * choice of fa_fwd_splitkv). */
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int n_splits);
 
 /* Forward attention, bf16, with the keys of every query tile split into
@@ -88,8 +89,12 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  * Same arguments, layouts and results as fa_fwd (up to rounding), plus
  * workspace: device memory of at least fa_fwd_splitkv_workspace_bytes(...)
  * bytes, 16-byte aligned, contents ignored on entry.
- * n_splits: 1..64 (FA_ERR_INVALID_ARG otherwise); ranges are balanced over
- * the key tiles each query tile actually visits (causal included). */
+ * n_splits: 1..64, or 0 to let the library choose (enough parts for the
+ * plain forward's B * Hq * ceil(N / 256) workgroups to cover the GPU's 256
+ * compute units, 1 when they already do, at most one part per 4 key tiles);
+ * FA_ERR_INVALID_ARG otherwise. Ranges are balanced over the key tiles each
+ * query tile actually visits (causal included). One part runs exactly
+ * fa_fwd (the workspace is then not touched). */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,

@@ -103,7 +103,15 @@ def test_splitkv_argument_errors():
     lib = _lib()
     ws = lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 3)
     assert ws >= 3 * (2 * 8 * 64 * 4 + 2 * 8 * 4)
-    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 0) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, -1) == 0
+    # n_splits = 0: the library's choice. 128 workgroups (B1 H4 N8192) -> 2 parts, 512 or more -> 1
+    one = lib.fa_fwd_splitkv_workspace_bytes(1, 4, 4, 8192, 128, 1)
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 4, 4, 8192, 128, 0) == lib.fa_fwd_splitkv_workspace_bytes(
+        1, 4, 4, 8192, 128, 2) > one
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 8, 8, 16384, 128, 0) == lib.fa_fwd_splitkv_workspace_bytes(
+        1, 8, 8, 16384, 128, 1)
+    # few key tiles: no more than one part per 4 of them (N = 8 -> 1 tile -> 1 part)
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 0) == lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 1)
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 64, 65) == 0
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 96, 2) == 0
 
@@ -117,7 +125,7 @@ def test_splitkv_argument_errors():
     assert call(d=96) == UNS
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 8, 256, 2) >= 2 * (2 * 8 * 256 * 4 + 2 * 8 * 4)
     assert call(d=256, ptrs=[NULL] * 6) == INV
-    assert call(splits=0) == INV
+    assert call(splits=-1) == INV
     assert call(splits=65) == INV
     assert call(wsb=ws - 1) == INV
     assert call(ptrs=[BAD] * 5 + [NULL]) == INV

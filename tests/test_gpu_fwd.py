@@ -194,6 +194,8 @@ SPLITKV = [
     (1, 2, 2, 17, 128, True, 5),
     (1, 1, 1, 1, 64, False, 2),
     (1, 2, 2, 300, 256, True, 3),
+    (1, 2, 2, 2048, 128, True, 0),   # n_splits = 0: the library's choice
+    (1, 1, 1, 300, 64, False, 0),
     (1, 2, 1, 1000, 256, False, 4),
 ]
 
@@ -211,6 +213,18 @@ def test_fwd_splitkv_small(B, Hq, Hkv, N, d, causal, n_splits):
     mx, mean = assert_bf16_close(to_f64(o), O, f"split-KV x{n_splits} O")
     assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
     _say(f"  split-KV x{n_splits}: O max {mx:.2e} mean {mean:.2e}")
+
+
+def test_fwd_splitkv_one_part_is_the_plain_forward():
+    import tiled_online_softmax_fa_amd as fa
+
+    inp = make_inputs(1, 8, 8, 4096, 128, "bf16", seed=17)
+    q, k, v = (to_device(inp, n, "bf16") for n in ("q", "k", "v"))
+    torch = torch_mod()
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd_splitkv(q, k, v, 1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_fwd_splitkv_long_sequence_16384():

@@ -182,9 +182,10 @@ def splitkv_workspace_bytes(B, Hq, Hkv, N, d, n_splits) -> int:
     return int(load_library().fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, n_splits))
 
 
-def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, out=None, lse=None, workspace=None):
+def fwd_splitkv(q, k, v, n_splits=0, causal=False, scale=None, out=None, lse=None, workspace=None):
     """Forward attention on bf16 tensors with each query tile's keys split into n_splits ranges
-    (separate workgroups, then a merge). Same results as fwd up to rounding. Returns (o, lse)."""
+    (separate workgroups, then a merge; 0 = the library's choice for the GPU's 256 compute units).
+    Same results as fwd up to rounding. Returns (o, lse)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, torch.bfloat16, n)

@@ -2,6 +2,7 @@
 // Every check that depends only on the arguments runs before any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -87,6 +88,18 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
 }
 
 constexpr int kMaxSplits = 64;
+constexpr int kComputeUnits = 256;  // MI355X
+
+// n_splits = 0: as many key-range parts as it takes for the workgroups of the
+// plain forward (one per query tile and head) to cover the compute units once,
+// at most one part per 4 key tiles of the longest query tile.
+int auto_splits(int B, int Hq, int N, int d) {
+  const int bm = d == 256 ? 128 : 256, bn = d == 256 ? 32 : 64;  // the forward's tiles
+  const long long n_wg = (long long)B * Hq * ((N + bm - 1) / bm);
+  int s = n_wg >= kComputeUnits ? 1 : (int)(kComputeUnits / n_wg);
+  s = std::min(s, std::max(1, ((N + bn - 1) / bn) / 4));
+  return std::max(1, std::min(s, kMaxSplits));
+}
 
 // split-KV workspace: o_part [S][rows][d] fp32, then (256-byte aligned) lse_part [S][rows] fp32
 size_t splitkv_o_bytes(int B, int Hq, int N, int d, int n_splits) {
@@ -120,6 +133,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int n_splits) {
   if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
+  if (n_splits == 0) n_splits = auto_splits(B, Hq, N, d);
   if (n_splits < 1 || n_splits > kMaxSplits) return 0;
   return splitkv_workspace(B, Hq, N, d, n_splits);
 }
@@ -129,6 +143,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream) {
   int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
   if (st != FA_OK) return st;
+  if (n_splits == 0) n_splits = auto_splits(B, Hq, N, d);
   if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   if (B == 0 || N == 0) return FA_OK;
   st = check_ptrs({q, k, v, o, lse, workspace});
@@ -147,6 +162,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   p.Hkv = Hkv;
   p.N = N;
   p.scale_log2 = scale * kLog2e;
+  // one part is the plain forward: no partial results, no merge
+  if (n_splits == 1) return launch_status(fa::launch_fwd_bf16(p, d, causal != 0, stream));
   p.n_splits = n_splits;
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + splitkv_o_bytes(B, Hq, N, d, n_splits));
