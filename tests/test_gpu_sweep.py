@@ -1,0 +1,55 @@
+"""Seeded random sweep of shapes through the forward and backward, against the fp64 oracle:
+ragged sequence lengths from 1 to 1300, every head dim, grouped heads, causal or not."""
+import sys
+
+import numpy as np
+import pytest
+
+from fa_inputs import make_inputs
+from fa_testlib import LSE_MAX_ABS, assert_bf16_close, errors, to_device, to_f64, torch_mod
+from oracle import attention_bwd, attention_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 3, 4]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.choice([int(rng.integers(1, 80)), int(rng.integers(80, 1300))]))
+        causal = bool(rng.integers(0, 2))
+        out.append((B, Hkv * G, Hkv, N, d, causal, 1000 + i))
+    return out
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,seed", _cases(16, 2026))
+def test_sweep_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
+    import tiled_online_softmax_fa_amd as fa
+
+    _say(f"sweep B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    inp = make_inputs(B, Hq, Hkv, N, d, "bf16", seed=seed, backward=True)
+    scale = d ** -0.5
+    q, k, v, dO = (to_device(inp, n, "bf16") for n in ("q", "k", "v", "dO"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dO, causal=causal, scale=scale)
+    torch_mod().cuda.synchronize()
+    O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    assert_bf16_close(to_f64(o), O, "O")
+    assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], causal, scale)
+    for name, got, rf in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        s = float(np.abs(rf).max())
+        g = to_f64(got)
+        if s == 0.0:
+            assert np.all(g == 0), name
+        else:
+            assert_bf16_close(g, rf, name, scale=s)
