@@ -111,10 +111,11 @@ size_t splitkv_workspace(int B, int Hq, int N, int d, int n_splits) {
   return splitkv_o_bytes(B, Hq, N, d, n_splits) + ((rows * sizeof(float) * (size_t)n_splits + 255) & ~(size_t)255);
 }
 
+// per query row: D_i, then (256-byte aligned) lse_i * log2(e)
+size_t bwd_row_bytes(int B, int Hq, int N) { return ((size_t)B * Hq * N * sizeof(float) + 255) & ~(size_t)255; }
 size_t bwd_workspace(int B, int Hq, int N, int d) {
-  const size_t rows = (size_t)B * Hq * N;
   (void)d;
-  return (rows * sizeof(float) + 255) & ~(size_t)255;  // D_i per query row
+  return 2 * bwd_row_bytes(B, Hq, N);
 }
 
 }  // namespace
@@ -274,6 +275,7 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   p.dv = dv;
   const size_t rows = (size_t)B * Hq * N;
   p.delta = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + bwd_row_bytes(B, Hq, N));
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -15,7 +15,7 @@
 //      forward kernel: Q and dO stay in registers and K, V tiles stream
 //      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
 //      accumulates dQ^T += K^T dS^T. Its prologue also forms the row term D
-//      of its rows (fp32) and writes it for kernel 2. Recomputing S and dP
+//      of its rows (fp32) and writes it, with lse in log2 units, for kernel 2. Recomputing S and dP
 //      here costs two more matrix products per tile than accumulating dQ
 //      inside kernel 2, but kernel 2 would have to add every key tile's
 //      contribution to dQ in memory (the atomics of "Flash Attention V3技术
@@ -140,10 +140,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const void* base = which ? (const void*)((const __bf16*)p.dout + qh * D) : (const void*)((const __bf16*)p.q + qh * D);
       copy16_global_to_lds_async(base, (uint32_t)(grow * D + lch * 8) * 2, dst + which * QT_BYTES + pp * 1024);
     }
-    // lse (waves 0-3) or D (waves 4-7): LPW rows per wave, one dword per lane
+    // lse * log2(e) (waves 0-3) or D (waves 4-7): LPW rows per wave, one dword per lane
     if (lane < LPW) {
       const int row = min(tq * BMQ + LPW * pair + lane, N - 1);
-      const float* src = (role == 0 ? p.lse : p.delta) + qh;
+      const float* src = (role == 0 ? p.lse2 : p.delta) + qh;
       copy4_global_to_lds_async(src, (uint32_t)row * 4, dst + (role == 0 ? LSE_OFF : DEL_OFF) + 4 * LPW * pair);
     }
   };
@@ -172,7 +172,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     for (int kb = 0; kb < KB; ++kb) acc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const float c = p.scale_log2;
-  constexpr float kLog2e = 1.4426950408889634f;
   int r_off[Swz::kDC];  // row-wise read: row L of a 16-row block, chunk dc*4 + g
 #pragma unroll
   for (int dc = 0; dc < Swz::kDC; ++dc) r_off[dc] = L * RB + (((dc * 4 + g) ^ Swz::f(L)) << 4);
@@ -237,7 +236,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int qq = q0 + cc * 32 + qb * 16 + r;  // query - 4g
             x = (qq >= lo[kb] && qq <= hi) ? x : kNegInf;
           }
-          e[r] = exp2_fast(fmaf(x, c, -l4[r] * kLog2e));
+          e[r] = exp2_fast(fmaf(x, c, -l4[r]));
         }
         pw[kb][2 * qb] = pack_bf16x2(e[0], e[1]);
         pw[kb][2 * qb + 1] = pack_bf16x2(e[2], e[3]);
@@ -449,7 +448,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
     }
     lse2[qb] = p.lse[qh + row] * 1.4426950408889634f;
     dl[qb] = sum_over_row_groups(dsum);  // the four lanes of the row hold its four d-slices
-    if (g == 0 && qw0 + qb * 16 + L < N) p.delta[qh + row] = dl[qb];  // for the dK/dV kernel
+    if (g == 0 && qw0 + qb * 16 + L < N) {  // for the dK/dV kernel
+      p.delta[qh + row] = dl[qb];
+      p.lse2[qh + row] = lse2[qb];
+    }
   }
   f32x4 acc[DB][QB];
 #pragma unroll
