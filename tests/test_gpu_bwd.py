@@ -160,3 +160,13 @@ def test_bwd_errors():
     zl = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda:0")
     dq, dk, dv = fa.bwd(z, z, z, z, zl, z)
     assert dq.shape == z.shape
+
+
+@pytest.mark.parametrize("scale,causal,d", [(0.37, True, 128), (1.0, False, 64), (0.02, True, 256)])
+def test_bwd_other_scales(scale, causal, d):
+    # scale enters both the exponent and the dQ / dK factor: a mix-up shows only away from 1/sqrt(d)
+    _say(f"bwd scale {scale} causal={causal} d{d}")
+    inp = make_inputs(1, 4, 2, 300, d, "bf16", seed=71, backward=True)
+    got = [to_f64(t) for t in _run(inp, causal, scale)]
+    ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], causal, scale)
+    _check_grads(got, ref, f"bwd scale {scale}")

@@ -6,19 +6,16 @@ import numpy as np
 import pytest
 
 from fa_inputs import bf16_bits_to_f32, bf16_round_bits, make_inputs
-from fa_testlib import LSE_MAX_ABS, assert_bf16_close, errors, to_device, to_f64, torch_mod
+from fa_testlib import (assert_bf16_close, assert_lse_close, errors, lse_bound, lse_bound_rows, to_device, to_f64,
+                        torch_mod)
 from oracle import (attention_fwd, attention_fwd_fp8, attention_fwd_rows, dequantize_blockwise_e4m3,
                     quantize_blockwise_e4m3)
 
 pytestmark = pytest.mark.gpu
 
-# lse of the FP8 path: the error of the FP8 matrix instruction's sums grows with the size of the scores
-# (measured about 3e-5 of |lse| with q scaled by 8), so the lse bound is LSE_MAX_ABS relative to max(1, |lse|)
-FP8_LSE_REL = LSE_MAX_ABS
-
-
-def _lse_ok(got, ref):
-    return np.all(np.abs(got - ref) <= FP8_LSE_REL * np.maximum(1.0, np.abs(ref)))
+# lse of the FP8 path: the same derived per-row bound as the bf16 path (fa_testlib.lse_bound), taken on the
+# dequantised Q and K that the oracle uses: the FP8 instruction's sums err in proportion to the sum of the
+# products' magnitudes, like the bf16 ones.
 
 
 def _say(*a):
@@ -95,8 +92,7 @@ def test_fwd_fp8_small(B, Hq, Hkv, N, d, causal):
     o, lse = _run_fp8(qc, qs, kc, ks, inp, causal, scale)
     O, LSE = attention_fwd_fp8(qc, qs, kc, ks, inp["v"], causal, scale)
     mx, mean = assert_bf16_close(o, O, "O (fp8 inputs)")
-    lmx = errors(lse, LSE)[0]
-    assert _lse_ok(lse, LSE), f"lse max {lmx:.2e}"
+    lmx = assert_lse_close(lse, LSE, lse_bound(dequantize_blockwise_e4m3(qc, qs), dequantize_blockwise_e4m3(kc, ks), scale))
     # the quantisation itself, against the unquantised inputs (reported; loose sanity bound)
     O0, _ = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
     qmx, qmean = errors(o, O0)
@@ -117,7 +113,9 @@ def test_fwd_fp8_peaky_with_gpu_quantised_inputs():
     O, LSE = attention_fwd_fp8(qc.cpu().numpy(), qs.cpu().numpy(), kc.cpu().numpy(), ks.cpu().numpy(), inp["v"],
                                True, 128 ** -0.5)
     assert_bf16_close(to_f64(o), O, "peaky fp8")
-    assert _lse_ok(to_f64(lse), LSE), f"lse max {errors(to_f64(lse), LSE)[0]:.2e}"
+    qd = dequantize_blockwise_e4m3(qc.cpu().numpy(), qs.cpu().numpy())
+    kd = dequantize_blockwise_e4m3(kc.cpu().numpy(), ks.cpu().numpy())
+    assert_lse_close(to_f64(lse), LSE, lse_bound(qd, kd, 128 ** -0.5))
 
 
 def test_fwd_fp8_workload_causal_4096():
@@ -136,7 +134,8 @@ def test_fwd_fp8_workload_causal_4096():
             Or, Lr = attention_fwd_rows(qd, kd, inp["v"], True, d ** -0.5, b, h, rows)
             mx = errors(o[b, h, rows], Or)[0]
             worst = max(worst, mx)
-            assert mx <= 2e-2 and _lse_ok(lse[b, h, rows], Lr)
+            assert mx <= 2e-2
+            assert_lse_close(lse[b, h, rows], Lr, lse_bound_rows(qd[b, h][rows], kd[b, h], d ** -0.5))
     _say(f"  sampled rows worst max {worst:.2e}")
 
 
@@ -152,3 +151,11 @@ def test_fwd_fp8_errors():
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         fa.fwd_fp8(c, torch.ones((1, 2, 2), dtype=torch.float32, device="cuda:0"), c, s, v)
+
+
+def test_fwd_fp8_other_scale_ragged_causal():
+    inp, qc, qs, kc, ks = _fp8_inputs(1, 4, 2, 333, 128, seed=5)
+    o, lse = _run_fp8(qc, qs, kc, ks, inp, True, 0.3)
+    O, LSE = attention_fwd_fp8(qc, qs, kc, ks, inp["v"], True, 0.3)
+    assert_bf16_close(o, O, "fp8 scale 0.3")
+    assert_lse_close(lse, LSE, lse_bound(dequantize_blockwise_e4m3(qc, qs), dequantize_blockwise_e4m3(kc, ks), 0.3))

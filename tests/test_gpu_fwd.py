@@ -5,8 +5,8 @@ import numpy as np
 import pytest
 
 from fa_inputs import WORKLOADS, make_inputs, make_workload_inputs
-from fa_testlib import (F32_MAX_ABS, LSE_MAX_ABS, assert_bf16_close, errors, run_fwd, to_device, to_f64,
-                        torch_mod)
+from fa_testlib import (F32_MAX_ABS, assert_bf16_close, assert_lse_close, errors, lse_bound, lse_bound_rows,
+                        run_fwd, to_device, to_f64, torch_mod)
 from oracle import attention_fwd, attention_fwd_rows
 
 pytestmark = pytest.mark.gpu
@@ -50,9 +50,8 @@ def test_fwd_bf16_small(B, Hq, Hkv, N, d, causal):
     inp, o, lse, scale = run_fwd(B, Hq, Hkv, N, d, causal, "bf16", seed=N + d)
     O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
     mx, mean = assert_bf16_close(o, O, "O")
-    lmx, _ = errors(lse, LSE)
+    lmx = assert_lse_close(lse, LSE, lse_bound(inp["q"], inp["k"], scale))
     _say(f"  O max {mx:.2e} mean {mean:.2e}  lse max {lmx:.2e}")
-    assert lmx <= LSE_MAX_ABS
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -64,7 +63,7 @@ def test_fwd_bf16_peaky_scores(causal, d):
     inp, o, lse, scale = run_fwd(1, 4, 2, 700, d, causal, "bf16", seed=11, q_mult=8.0)
     O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
     assert_bf16_close(o, O, "O")
-    assert errors(lse, LSE)[0] <= LSE_MAX_ABS * 8
+    assert_lse_close(lse, LSE, lse_bound(inp["q"], inp["k"], scale))
 
 
 def test_fwd_bf16_increasing_keys_force_rescales():
@@ -88,7 +87,7 @@ def test_fwd_bf16_increasing_keys_force_rescales():
         torch.cuda.synchronize()
         O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, 0.05)
         assert_bf16_close(to_f64(o), O, f"O causal={causal}")
-        assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS * 10
+        assert_lse_close(to_f64(lse), LSE, lse_bound(inp["q"], inp["k"], 0.05))
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 1, 1, 256, 64, False), (1, 2, 2, 300, 64, True),
@@ -129,7 +128,7 @@ def test_fwd_bf16_workload_multihead_2048_full():
     O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
     mx, mean = assert_bf16_close(to_f64(o), O, "O")
     _say(f"  O max {mx:.2e} mean {mean:.2e}")
-    assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
+    assert_lse_close(to_f64(lse), LSE, lse_bound(inp["q"], inp["k"], w.scale))
 
 
 def _sampled_check(w, n_full_heads=2, rows_per_head=48, seed=123):
@@ -150,14 +149,16 @@ def _sampled_check(w, n_full_heads=2, rows_per_head=48, seed=123):
             mx, _ = errors(o[b, h, rows], Or)
             worst = max(worst, mx)
             assert mx <= 2e-2, f"head ({b},{h}) sampled rows: max {mx:.3e}"
-            assert errors(lse[b, h, rows], Lr)[0] <= LSE_MAX_ABS
+            assert_lse_close(lse[b, h, rows], Lr,
+                             lse_bound_rows(inp["q"][b, h][rows], inp["k"][b, h // (w.Hq // w.Hkv)], w.scale))
     G = w.Hq // w.Hkv
     for i in range(n_full_heads):
         b, h = i % w.B, (7 * i + 3) % w.Hq
         O, LSE = attention_fwd(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h // G:h // G + 1],
                                inp["v"][b:b + 1, h // G:h // G + 1], w.causal, w.scale)
         assert_bf16_close(o[b:b + 1, h:h + 1], O, f"full head ({b},{h})")
-        assert errors(lse[b:b + 1, h:h + 1], LSE)[0] <= LSE_MAX_ABS
+        assert_lse_close(lse[b:b + 1, h:h + 1], LSE,
+                         lse_bound(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h // G:h // G + 1], w.scale))
     _say(f"  sampled worst max {worst:.2e}")
 
 
@@ -195,6 +196,7 @@ SPLITKV = [
     (1, 1, 1, 1, 64, False, 2),
     (1, 2, 2, 300, 256, True, 3),
     (1, 2, 2, 2048, 128, True, 0),   # n_splits = 0: the library's choice
+    (1, 2, 1, 1500, 256, False, 0),
     (1, 1, 1, 300, 64, False, 0),
     (1, 2, 1, 1000, 256, False, 4),
 ]
@@ -211,7 +213,7 @@ def test_fwd_splitkv_small(B, Hq, Hkv, N, d, causal, n_splits):
     torch_mod().cuda.synchronize()
     O, LSE = attention_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
     mx, mean = assert_bf16_close(to_f64(o), O, f"split-KV x{n_splits} O")
-    assert errors(to_f64(lse), LSE)[0] <= LSE_MAX_ABS
+    assert_lse_close(to_f64(lse), LSE, lse_bound(inp["q"], inp["k"], scale))
     _say(f"  split-KV x{n_splits}: O max {mx:.2e} mean {mean:.2e}")
 
 
@@ -241,7 +243,7 @@ def test_fwd_splitkv_long_sequence_16384():
         rows = np.unique(np.concatenate([[0, 1, 255, 256, w.N - 1], rng.integers(0, w.N, 24)]))
         Or, Lr = attention_fwd_rows(inp["q"], inp["k"], inp["v"], True, w.scale, 0, h, rows)
         assert errors(o[0, h, rows], Or)[0] <= 2e-2
-        assert errors(lse[0, h, rows], Lr)[0] <= LSE_MAX_ABS
+        assert_lse_close(lse[0, h, rows], Lr, lse_bound_rows(inp["q"][0, h][rows], inp["k"][0, h // 2], w.scale))
 
 
 def test_fwd_bf16_is_bitwise_repeatable():
