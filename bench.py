@@ -19,7 +19,6 @@ import argparse
 import ctypes
 import hashlib
 import json
-import math
 import os
 import platform
 import sys

@@ -5,7 +5,7 @@ import sys
 import numpy as np
 import pytest
 
-from fa_testlib import assert_bf16_close, assert_lse_close, errors, lse_bound_rows, to_f64, torch_mod
+from fa_testlib import assert_bf16_close, assert_lse_close, errors, lse_bound_rows, torch_mod
 from oracle import attention_bwd, attention_fwd_rows
 
 pytestmark = pytest.mark.gpu

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import make_block_mask, make_inputs
-from fa_testlib import assert_bf16_close, assert_lse_close, errors, lse_bound, to_device, to_f64, torch_mod
+from fa_testlib import assert_bf16_close, assert_lse_close, lse_bound, to_device, to_f64, torch_mod
 from oracle import attention_fwd, attention_fwd_blockmask
 
 pytestmark = pytest.mark.gpu
