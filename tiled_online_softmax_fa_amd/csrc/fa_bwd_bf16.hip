@@ -36,21 +36,26 @@ namespace fa {
 //
 // Tiles here are read both row-wise (16-byte reads of one row's chunk) and
 // transposed (ds_read_b64_tr_b16), so the 16-byte chunk c of row r is stored
-// at chunk c ^ f(r), with f chosen so that both access patterns spread over
-// the banks: f maps the 8 (16) consecutive rows of a row-wise read to
-// distinct chunks, and the rows 4g..4g+3 of a transposed read (two adjacent
-// chunks each) to 8 distinct chunks. f < 16 only permutes chunks inside one
-// 256-byte bank sweep, so with 512-byte rows (d = 256) chunk c + 16 sits
-// 256 bytes after chunk c: the fragment offsets of the second half of a row
-// are those of the first plus 256 (kHalfRow below), a constant.
+// at chunk c ^ f(r). Over one 256-byte bank sweep, f must send the 16 rows of
+// a row-wise read (16 lanes per cycle, one chunk each) to 16 distinct
+// 16-byte slots, and the rows 0..7 (8..15) of a transposed read (32 lanes per
+// cycle, rows 4g..4g+3 of two lane groups, 32 bytes per row, i.e. two
+// adjacent chunks whose pair index is c/2 ^ f(r)/2) to 8 distinct 32-byte
+// slots. With one row per sweep (d >= 128) f(r) = (r mod 8) * 2 + bit 3 of r
+// does both; with two 128-byte rows per sweep (d = 64) the same on r / 2,
+// since the row's half of the sweep is already fixed by r mod 2. f < 16 only
+// permutes chunks inside one 256-byte bank sweep, so with 512-byte rows
+// (d = 256) chunk c + 16 sits 256 bytes after chunk c: the fragment offsets of
+// the second half of a row are those of the first plus 256 (kHalfRow below),
+// a constant. f repeats every 16 rows, as the fragment reads add whole
+// 16-row blocks.
 template <int D>
 struct DualSwizzle {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = kRowBytes / 16;
   __device__ static __forceinline__ int f(int row) {
-    int x = ((row & 3) << 1) | ((row >> 2) & 1);
-    if (kChunks >= 16) x |= ((row >> 3) & 1) << 3;
-    return x;
+    const int r = kChunks >= 16 ? row : row >> 1;
+    return kChunks >= 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
   }
   // lane offsets kept per 32-column step (row-wise reads) and per 16-column
   // block (transposed reads) within one 256-byte half row
