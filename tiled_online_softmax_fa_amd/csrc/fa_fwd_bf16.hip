@@ -177,6 +177,35 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int q0 = tc.tile * BM;
   const int qw0 = q0 + wave * QPW;  // first query row of this wave
 
+  // Q^T fragments (B operand of S^T = K Q^T), held for the whole key loop.
+  bf16x8 qf[F8 ? 1 : QB][F8 ? 1 : DC];
+  i32x8 qf8[F8 ? QB : 1][F8 ? DC8 : 1];  // F8: bytes 32 g .. 32 g + 31 of each 128-byte k-step
+  auto load_q = [&]() __attribute__((always_inline)) {
+    if constexpr (F8) {
+      const unsigned char* q8 = (const unsigned char*)p.q + ((size_t)(b * p.Hq + h) * N) * D;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = min(qw0 + qb * 16 + L, N - 1);
+#pragma unroll
+        for (int dc = 0; dc < DC8; ++dc) {
+          const u32x4* src = (const u32x4*)(q8 + (size_t)row * D + dc * 128 + g * 32);
+          const u32x4 lo = src[0], hi = src[1];
+          qf8[qb][dc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = min(qw0 + qb * 16 + L, N - 1);
+        const u32x4* src = (const u32x4*)(qg + (size_t)row * D + g * 8);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) qf[qb][dc] = __builtin_bit_cast(bf16x8, src[dc * 4]);
+      }
+    }
+  };
+  // sparse: the Q loads go out first, so their latency overlaps the mask scan
+  if constexpr (SPARSE) load_q();
+
   // sparse: compact the listed key blocks (ballot + prefix over the waves)
   int n_list = 0;
   if constexpr (SPARSE) {
@@ -276,31 +305,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   };
 
   for (int t = t_lo; t < t_lo + STAGES - 1 && t < n_kv; ++t) issue_tile_copy(t);
-
-  // Q^T fragments (B operand of S^T = K Q^T), held for the whole key loop.
-  bf16x8 qf[F8 ? 1 : QB][F8 ? 1 : DC];
-  i32x8 qf8[F8 ? QB : 1][F8 ? DC8 : 1];  // F8: bytes 32 g .. 32 g + 31 of each 128-byte k-step
-  if constexpr (F8) {
-    const unsigned char* q8 = (const unsigned char*)p.q + ((size_t)(b * p.Hq + h) * N) * D;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = min(qw0 + qb * 16 + L, N - 1);
-#pragma unroll
-      for (int dc = 0; dc < DC8; ++dc) {
-        const u32x4* src = (const u32x4*)(q8 + (size_t)row * D + dc * 128 + g * 32);
-        const u32x4 lo = src[0], hi = src[1];
-        qf8[qb][dc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-    }
-  } else {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = min(qw0 + qb * 16 + L, N - 1);
-      const u32x4* src = (const u32x4*)(qg + (size_t)row * D + g * 8);
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) qf[qb][dc] = __builtin_bit_cast(bf16x8, src[dc * 4]);
-    }
-  }
+  if constexpr (!SPARSE) load_q();
 
   f32x4 acc[DB][QB];
 #pragma unroll
