@@ -131,6 +131,11 @@ def test_splitkv_argument_errors():
     assert call(ptrs=[BAD] * 5 + [NULL]) == INV
     assert call(Hq=3, Hkv=2) == INV
     assert call(B=0, ptrs=[NULL] * 6, wsb=0) == FA_OK
+    # empty problems with the automatic part count (no division by an empty grid)
+    assert call(B=0, ptrs=[NULL] * 6, wsb=0, splits=0) == FA_OK
+    assert call(N=0, ptrs=[NULL] * 6, wsb=0, splits=0) == FA_OK
+    assert lib.fa_fwd_splitkv_workspace_bytes(0, 2, 2, 8, 64, 0) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 0, 64, 0) == 0
 
 
 def test_blocksparse_argument_errors():

@@ -96,6 +96,7 @@ constexpr int kComputeUnits = 256;  // MI355X
 int auto_splits(int B, int Hq, int N, int d) {
   const int bm = d == 256 ? 128 : 256, bn = d == 256 ? 32 : 64;  // the forward's tiles
   const long long n_wg = (long long)B * Hq * ((N + bm - 1) / bm);
+  if (n_wg <= 0) return 1;  // empty problem
   int s = n_wg >= kComputeUnits ? 1 : (int)(kComputeUnits / n_wg);
   s = std::min(s, std::max(1, ((N + bn - 1) / bn) / 4));
   return std::max(1, std::min(s, kMaxSplits));
