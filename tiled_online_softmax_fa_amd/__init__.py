@@ -121,6 +121,16 @@ def _stream_ptr(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _guard(*tensors):
+    """All tensors on one GPU; the calls below run with that GPU current (the library's device check and
+    launches use the current device)."""
+    torch = _torch()
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+    return torch.cuda.device(devs.pop())
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
@@ -162,7 +172,8 @@ def _fwd_impl(entry, dtype, q, k, v, causal, scale, out, lse):
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("out/lse have the wrong shape")
     lib = load_library()
-    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+    with _guard(q, k, v, out, lse):
+        st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
                              int(bool(causal)), float(scale), _stream_ptr(q))
     _check(st, entry)
     return out, lse
@@ -204,8 +215,9 @@ def fwd_splitkv(q, k, v, n_splits=0, causal=False, scale=None, out=None, lse=Non
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     lib = load_library()
-    st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), int(n_splits), _stream_ptr(q))
+    with _guard(q, k, v, out, lse, workspace):
+        st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                B, Hq, Hkv, N, d, int(bool(causal)), float(scale), int(n_splits), _stream_ptr(q))
     _check(st, "fa_fwd_splitkv")
     return out, lse
 
@@ -230,7 +242,8 @@ def quantize_fp8(x, codes=None, scale=None):
     _require(scale, torch.float32, "scale")
     if tuple(codes.shape) != (B, H, N, d) or tuple(scale.shape) != (B, H, nb):
         raise ValueError("codes/scale have the wrong shape")
-    st = load_library().fa_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scale), B, H, N, d, _stream_ptr(x))
+    with _guard(x, codes, scale):
+        st = load_library().fa_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scale), B, H, N, d, _stream_ptr(x))
     _check(st, "fa_quantize_fp8")
     return codes, scale
 
@@ -258,7 +271,8 @@ def fwd_fp8(q_codes, q_scale, k_codes, k_scale, v, causal=False, scale=None, out
     _require(lse, torch.float32, "lse")
     if tuple(out.shape) != (B, Hq, N, d) or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("out/lse have the wrong shape")
-    st = load_library().fa_fwd_fp8(_ptr(q_codes), _ptr(k_codes), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(out),
+    with _guard(q_codes, k_codes, v, q_scale, k_scale, out, lse):
+        st = load_library().fa_fwd_fp8(_ptr(q_codes), _ptr(k_codes), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(out),
                                    _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_ptr(v))
     _check(st, "fa_fwd_fp8")
     return out, lse
@@ -309,8 +323,9 @@ def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, lse
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("out/lse have the wrong shape")
     lib = load_library()
-    st = lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(m), sb, sh, B, Hq, Hkv, N, d,
-                                int(bool(causal)), float(scale), _stream_ptr(q))
+    with _guard(q, k, v, out, lse, m):
+        st = lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(m), sb, sh, B, Hq, Hkv, N, d,
+                                    int(bool(causal)), float(scale), _stream_ptr(q))
     _check(st, "fa_fwd_blocksparse")
     return out, lse
 
@@ -347,10 +362,11 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
     lib = load_library()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_ptr(q))
-    if events is None:
-        _check(lib.fa_bwd(*args), "fa_bwd")
-    else:
-        _check(lib.fa_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p)), "fa_bwd_timed")
+    with _guard(q, k, v, o, dout, lse, dq, dk, dv, workspace):
+        if events is None:
+            _check(lib.fa_bwd(*args), "fa_bwd")
+        else:
+            _check(lib.fa_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p)), "fa_bwd_timed")
     return dq, dk, dv
 
 
