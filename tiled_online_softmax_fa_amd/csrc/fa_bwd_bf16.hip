@@ -554,6 +554,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
   // Two loops: tiles before t_mask need no mask in any wave (straight-line
   // bodies), the rest (the workgroup's diagonal and the end of the sequence)
   // take the masked path per wave.
+  // Every load of the prologue landed before the key loop. The compiler counts
+  // the Q/dO/O/lse loads but not the tile copies (inline assembly), so unless
+  // a full wait covers them on every path into the loop it waits for them
+  // inside the loop, which in fact holds each wave, on every tile, until its
+  // newest copy has landed. (The D computation above has waited for nearly
+  // all of them already.)
+  wait_vmcnt0();
   int stage = 0;
   auto begin_tile = [&](int t) __attribute__((always_inline)) {
     if (t + STAGES - 2 < n_kv) {

@@ -287,7 +287,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       // the tile's K scale (every wave copies it, so all waves count the same copies)
       if (lane == 0) {
         const float* ks = p.k_descale + (size_t)(b * p.Hkv + hk) * ((N + kFp8Block - 1) / kFp8Block);
-        copy4_global_to_lds_async(ks, (uint32_t)(kv0 / kFp8Block) * 4, kdst + SCALE_OFF);
+        copy4_global_to_lds_async(ks, (uint32_t)(min(kv0, N - 1) / kFp8Block) * 4, kdst + SCALE_OFF);
       }
       return;
     }
@@ -556,12 +556,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     if (t + STAGES - 1 < n_kv) issue_tile_copy(t + STAGES - 1);
   };
+  // Q and the first STAGES-1 tiles landed, on every path into the key loop.
+  // The compiler counts the Q loads but not the copies (inline assembly), so
+  // to it the Q loads are the newest ones, covered only by a full wait; a
+  // path left without one (even an infeasible one of its control flow) makes
+  // it wait for Q inside the loop, which in fact holds each wave, on every
+  // tile, until its newest copy has landed. The prologue tiles are issued
+  // together, so waiting for the second costs little.
+  wait_vmcnt0();
   if (n_kv > t_lo) {
-    if (n_kv - t_lo >= STAGES - 1) {
-      wait_vmcnt_le<(STAGES - 2) * OPS>();  // tile 0 landed; tiles 1..STAGES-2 may still fly
-    } else {
-      wait_vmcnt0();
-    }
     __syncthreads();
     if constexpr (SPARSE) {
       // (the first chunk's scores; the loop below consumes them)
