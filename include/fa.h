@@ -164,8 +164,8 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  * heads dk and dv sum over the query heads that read each key/value head.
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, contents ignored on entry (float32 scratch for the row
- * term D_i = sum_c dout_ic o_ic and for lse_i * log2 e, both written by the
- * first kernel for the second). All three outputs are bitwise repeatable
+ * term, stored negated as -D_i = -sum_c dout_ic o_ic, and for lse_i * log2 e,
+ * both written by the first kernel for the second). All three outputs are bitwise repeatable
  * (no atomics). Supported d: 64, 128, 256. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,

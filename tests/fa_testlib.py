@@ -103,3 +103,29 @@ def run_fwd(B, Hq, Hkv, N, d, causal, dtype="bf16", seed=0, q_mult=1.0, scale=No
     o, lse = fn(q, k, v, causal=causal, scale=scale)
     torch_mod().cuda.synchronize()
     return inp, to_f64(o), to_f64(lse), scale
+
+
+def zero_grad_bounds(inp, scale):
+    """Bounds on |dQ| and |dK| where the exact gradient is zero (e.g. one key).
+
+    There dS = P o (dP - D) is exactly 0, and the kernels form dP - D as an fp32
+    matrix product whose accumulator starts at -D, i.e. the difference of two
+    fp32 sums of the same d products dO_ic v_jc (D from the stored O). Each sum
+    errs by at most d 2^-24 times its sum of magnitudes, so
+    |dS_ij| <= E_ij = 2 d 2^-24 sum_c |dO_ic| (|v_jc| + max_j' |v_j'c|) (P <= 1, |O| <= max |V|),
+    and dQ = scale dS K, dK = scale dS^T Q carry it to
+    |dQ_ic| <= scale sum_j E_ij |k_jc|,  |dK_jc| <= scale sum_i E_ij |q_ic|
+    (per batch and head; grouped heads sum dK over the group; all heads are
+    bounded with the group's K/V head).
+    """
+    q, k, v, dO = (np.abs(inp[n].astype(np.float64)) for n in ("q", "k", "v", "dO"))
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    bq, bk = np.zeros_like(q), np.zeros_like(k)
+    for b in range(B):
+        for h in range(Hq):
+            vv, kk = v[b, h // G], k[b, h // G]
+            E = 2 * d * 2.0 ** -24 * (dO[b, h] @ (vv + vv.max(axis=0)).T)  # [N queries, N keys]
+            bq[b, h] = scale * E @ kk
+            bk[b, h // G] += scale * E.T @ q[b, h]
+    return bq, bk

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import WORKLOADS, make_inputs, make_workload_inputs
-from fa_testlib import assert_bf16_close, to_device, to_f64, torch_mod
+from fa_testlib import assert_bf16_close, to_device, to_f64, torch_mod, zero_grad_bounds
 from oracle import attention_bwd, attention_bwd_head
 
 pytestmark = pytest.mark.gpu
@@ -26,13 +26,20 @@ def _run(inp, causal, scale):
     return dq, dk, dv
 
 
-def _check_grads(got, ref, what):
+def _check_grads(got, ref, what, inp=None, scale=None):
     worst = []
+    zero_bounds = None
     for name, gt, rf in zip(("dQ", "dK", "dV"), got, ref):
         s = float(np.abs(rf).max())
-        if s == 0.0:  # an exactly-zero gradient (e.g. a single key) must come out exactly zero
-            assert np.all(gt == 0), f"{what} {name}: expected exact zeros"
-            worst.append(f"{name} exact 0")
+        if s == 0.0:  # an exactly-zero gradient (e.g. a single key): fp32 rounding of dP - D only
+            assert inp is not None, f"{what} {name}: zero reference needs the inputs for its bound"
+            if zero_bounds is None:
+                zero_bounds = zero_grad_bounds(inp, scale)
+            bound = zero_bounds[0] if name == "dQ" else zero_bounds[1]
+            assert name != "dV" and np.all(np.abs(gt) <= bound), (
+                f"{what} {name}: |got| up to {np.abs(gt).max():.3e} where the exact gradient is 0 "
+                f"(bound {bound.max():.3e})")
+            worst.append(f"{name} {np.abs(gt).max():.1e} (exact 0)")
             continue
         mx, mean = assert_bf16_close(gt, rf, f"{what} {name}", scale=s)
         worst.append(f"{name} max {mx / s:.1e} mean {mean / s:.1e}")
@@ -67,7 +74,7 @@ def test_bwd_small(B, Hq, Hkv, N, d, causal):
     scale = d ** -0.5
     got = [to_f64(t) for t in _run(inp, causal, scale)]
     ref = attention_bwd(inp["q"], inp["k"], inp["v"], inp["dO"], causal, scale)
-    _check_grads(got, ref, "bwd")
+    _check_grads(got, ref, "bwd", inp, scale)
 
 
 def test_bwd_peaky():

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import make_inputs
-from fa_testlib import assert_bf16_close, assert_lse_close, lse_bound, to_device, to_f64, torch_mod
+from fa_testlib import assert_bf16_close, assert_lse_close, lse_bound, to_device, to_f64, torch_mod, zero_grad_bounds
 from oracle import attention_bwd, attention_fwd
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,9 @@ def test_sweep_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
     for name, got, rf in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         s = float(np.abs(rf).max())
         g = to_f64(got)
-        if s == 0.0:
-            assert np.all(g == 0), name
+        if s == 0.0:  # exact gradient 0 (one key): only the fp32 rounding of dP - D remains
+            assert name != "dV"
+            bound = zero_grad_bounds(inp, scale)[0 if name == "dQ" else 1]
+            assert np.all(np.abs(g) <= bound), name
         else:
             assert_bf16_close(g, rf, name, scale=s)

@@ -15,7 +15,7 @@
 //      forward kernel: Q and dO stay in registers and K, V tiles stream
 //      through an LDS ring; per 32-key chunk it recomputes S^T and dP^T and
 //      accumulates dQ^T += K^T dS^T. Its prologue also forms the row term D
-//      of its rows (fp32) and writes it, with lse in log2 units, for kernel 2. Recomputing S and dP
+//      of its rows (fp32) and writes -D, with lse in log2 units, for kernel 2. Recomputing S and dP
 //      here costs two more matrix products per tile than accumulating dQ
 //      inside kernel 2, but kernel 2 would have to add every key tile's
 //      contribution to dQ in memory (the atomics of "Flash Attention V3技术
@@ -73,6 +73,8 @@ struct DualSwizzle {
 // one SIMD (waves p and p + 4):
 //   wave A (p):     S = Q K^T, P = 2^(c S - lse log2 e) (masked), dV^T += dO^T P
 //   wave B (p + 4): dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
+// (both kernels start the dP accumulators at -D, so the matrix unit forms
+// dP - D and the vector unit only multiplies by P)
 // so each wave keeps one of K^T / V^T and one accumulator in registers.
 // Keys sit on the accumulator's columns: P and dS come out of the MFMA in
 // the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A
@@ -265,11 +267,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   auto chunk_b = [&](const lds_u8* st, int cc, const lds_u8* pb) __attribute__((always_inline)) {
     const lds_u8* qt = st;
     const lds_u8* dt = st + QT_BYTES;
-    f32x4 dp[QB][KB];
+    f32x4 dp[QB][KB];  // dP - D: the accumulators start at -D of their rows
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const f32x4 nd4 = *(const FA_LDS f32x4*)(st + DEL_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = nd4;
+    }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
@@ -286,15 +290,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const u32x4 pw = *(const FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const f32x4 d4 = *(const FA_LDS f32x4*)(st + DEL_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
         float e[4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const uint32_t w = pw[2 * qb + h2];
           const float p0 = __builtin_bit_cast(float, w << 16);
           const float p1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
-          e[2 * h2] = p0 * (dp[qb][kb][2 * h2] - d4[2 * h2]);
-          e[2 * h2 + 1] = p1 * (dp[qb][kb][2 * h2 + 1] - d4[2 * h2 + 1]);
+          e[2 * h2] = p0 * dp[qb][kb][2 * h2];
+          e[2 * h2 + 1] = p1 * dp[qb][kb][2 * h2 + 1];
         }
         dw[kb][2 * qb] = pack_bf16x2(e[0], e[1]);
         dw[kb][2 * qb + 1] = pack_bf16x2(e[2], e[3]);
@@ -454,7 +457,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
     lse2[qb] = p.lse[qh + row] * 1.4426950408889634f;
     dl[qb] = sum_over_row_groups(dsum);  // the four lanes of the row hold its four d-slices
     if (g == 0 && qw0 + qb * 16 + L < N) {  // for the dK/dV kernel
-      p.delta[qh + row] = dl[qb];
+      p.delta[qh + row] = -dl[qb];
       p.lse2[qh + row] = lse2[qb];
     }
   }
@@ -504,7 +507,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[qb] = f32x4{-dl[qb], -dl[qb], -dl[qb], -dl[qb]};  // dP^T - D
         }
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
@@ -522,7 +525,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) {
           float x = s[qb][r];
           if (decltype(mask)::value) x = (hb * 16 + r <= lim[qb] - ch * 32) ? x : kNegInf;
-          e[r] = exp2_fast(fmaf(x, c, -lse2[qb])) * (dp[qb][r] - dl[qb]);
+          e[r] = exp2_fast(fmaf(x, c, -lse2[qb])) * dp[qb][r];
         }
         half_pk[hb][qb] = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
       }
@@ -610,7 +613,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
   constexpr int BM_DQ = D == 256 ? 128 : 256, BN_DKDV = D == 256 ? 64 : 128;  // as in the kernels
   BwdParams p = p_in;
   hipError_t e;
-  // dQ first: it also writes the row term D that the dK/dV kernel reads
+  // dQ first: it also writes -D (the row term, negated) that the dK/dV kernel reads
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + BM_DQ - 1) / BM_DQ;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);

@@ -41,7 +41,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // [B, Hq, N] workspace: D_i = sum_c dout_ic o_ic
+  float* delta;   // [B, Hq, N] workspace: -D_i = -sum_c dout_ic o_ic (the dP accumulators start there)
   float* lse2;    // [B, Hq, N] workspace: lse_i * log2(e), written with D by the dQ kernel
   int B, Hq, Hkv, N;
   float scale;
