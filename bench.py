@@ -147,6 +147,8 @@ def time_configs(torch, min_warmup_s):
                           "compulsory_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
                           "source_digest": source_digest()}), flush=True)
 
+    time_short_sequences(torch, min_warmup_s)
+
     # head dim 256, and split-KV on shapes with few query tiles (seeded N(0,1) inputs, bf16): plain forward
     # vs key-range parts
     from fa_inputs import Workload
@@ -315,6 +317,56 @@ def time_configs(torch, min_warmup_s):
     return 0
 
 
+SHORT_SEQUENCES = ((64, 16, 128, 128), (32, 16, 256, 128), (16, 16, 512, 128))  # B, H, N, d: 16-32 MiB per tensor
+
+
+def time_short_sequences(torch, min_warmup_s):
+    """bf16 forward on short sequences, where each (batch, head) is one or two query tiles and the work per
+    byte is small: compulsory HBM bytes (Q, K, V read, O and lse written, each once) per second, against the
+    8 TB/s of HBM, next to the FLOP rate."""
+    import numpy as np
+
+    import tiled_online_softmax_fa_amd as fa
+    from fa_inputs import Workload, make_workload_inputs
+
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    for B, H, N, d in SHORT_SEQUENCES:
+        for causal in (False, True):
+            w = Workload(f"fwd_short_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}", B, H, H, N, d, "bf16", causal,
+                         seed=9)
+            inp = make_workload_inputs(w)
+            dev = {n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+                   for n in ("q", "k", "v")}
+            o = torch.empty_like(dev["q"])
+            lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+            t0 = time.perf_counter()
+            n = 0
+            while n < 20 or time.perf_counter() - t0 < min(min_warmup_s, 0.5):
+                fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, out=o, lse=lse)
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            K = 50
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(K):
+                fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, out=o, lse=lse)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            us = hip.ms(e0, e1) / K * 1e3
+            f_fwd, _ = flops(B, H, N, d, causal)
+            nbytes = 4 * B * H * N * d * 2 + 4 * B * H * N
+            gbs = nbytes / (us * 1e-6) / 1e9
+            tflops = f_fwd / (us * 1e-6) / 1e12
+            print(json.dumps({"workload": w.name, "entry": "fa_fwd", "avg_us": us, "compulsory_bytes": nbytes,
+                              "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS, "tflops": tflops,
+                              "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "source_digest": source_digest()}),
+                  flush=True)
+    return 0
+
+
 COPY_BYTES = 1 << 29  # 512 MiB read and 512 MiB written per calibration copy
 COPY_LAUNCHES = 4
 
@@ -424,6 +476,8 @@ def main():
                     help="keep warming up until this many seconds have passed (0 for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM byte counters)")
+    ap.add_argument("--short-seq", action="store_true",
+                    help="only the short-sequence forward cases of --configs (HBM-rate figures)")
     ap.add_argument("--configs", action="store_true",
                     help="only time the forward on every forward workload of fa_inputs.WORKLOADS, on head dim "
                          "256, split-KV, block-sparse and FP8 shapes, the FP8 quantiser, and the backward at head "
@@ -446,6 +500,8 @@ def main():
         return copy_calibration(torch)
     if args.configs:
         return time_configs(torch, args.min_warmup_s)
+    if args.short_seq:
+        return time_short_sequences(torch, args.min_warmup_s)
 
     import tiled_online_softmax_fa_amd as fa
     from fa_inputs import make_inputs

@@ -14,6 +14,9 @@
 //     waves per SIMD; each wave owns 32 consecutive query rows and never
 //     exchanges partial results with another wave (head dim 256: 128-row
 //     tiles, 16 rows per wave, so the accumulator keeps its register size);
+//   * short sequences (N <= 512, head dim <= 128): workgroups of 4 waves (128
+//     rows) with 32-key tiles, 48 KiB of LDS at head dim 128, so two
+//     workgroups share a CU and one's loads overlap the other's math;
 //   * K/V tiles of 64 keys (32 at head dim 256) are copied global -> LDS with 16-byte direct loads
 //     into a ring of STAGES stages. The copy of tile t+STAGES-1 is issued
 //     right after the single barrier that publishes tile t+1, so it overlaps
@@ -115,7 +118,7 @@ struct KVSwizzle {
 // "4.3 FlashAttention-2与FlashAttention-3演进", FlashAttention-3 section 2).
 template <int D, bool CAUSAL, int QPW, int NW, bool PRIO, int STAGES, bool SPLIT = false, int BN = 64,
           bool SPARSE = false, bool F8 = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(NW <= 4 ? 2 : 1)))
 void fa_fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = QPW * NW;
   static_assert(BN == 32 || BN == 64, "one or two 32-key chunks per tile");
@@ -728,8 +731,31 @@ struct FwdCfg {
   static constexpr int QPW = D == 256 ? 16 : 32, NW = 8, STAGES = 3, BN = D == 256 ? 32 : 64;
 };
 
+// Short sequences (a head's queries fill one or a few tiles, little work per
+// byte): 4-wave workgroups of 128 rows with 32-key tiles and registers kept
+// within 256 per wave, so two workgroups share a CU and one's loads overlap
+// the other's math.
+constexpr int kShortSeqMaxN = 512;
+struct FwdShortCfg {
+  static constexpr int QPW = 32, NW = 4, STAGES = 3, BN = 32;
+};
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_short(const FwdParams& p_in, hipStream_t stream) {
+  using C = FwdShortCfg;
+  FwdParams p = p_in;
+  p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
+  const unsigned grid = (unsigned)(p.n_tiles * p.B * p.Hq);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, C::QPW, C::NW, true, C::STAGES, false, C::BN>), dim3(grid),
+                     dim3(C::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream) {
+  if constexpr (D <= 128) {
+    if (p_in.N <= kShortSeqMaxN) return launch_fwd_bf16_short<D, CAUSAL>(p_in, stream);
+  }
   using C = FwdCfg<D>;
   FwdParams p = p_in;
   p.n_tiles = (p.N + C::QPW * C::NW - 1) / (C::QPW * C::NW);
