@@ -174,6 +174,18 @@ def test_fwd_bf16_workload_causal_gqa_4096():
     _sampled_check(w, rows_per_head=16)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(4, 32, 8, 1100, 128, True), (4, 32, 8, 1100, 128, False),
+                                                  (4, 32, 32, 1037, 64, False), (2, 64, 64, 777, 128, False)])
+def test_fwd_bf16_full_grid_ragged(B, Hq, Hkv, N, d, causal):
+    # grids of at least two 256-row workgroups per compute unit with N > 512 (and not causal d = 64) take the
+    # 256-row tiles; ragged lengths cut their last query tile and last key tile
+    from fa_inputs import Workload
+
+    w = Workload(f"fwd_grid_b{B}hq{Hq}hkv{Hkv}n{N}d{d}", B, Hq, Hkv, N, d, "bf16", causal, seed=N + d)
+    _say(f"{w.name} causal={causal} (sampled rows + full heads)")
+    _sampled_check(w, rows_per_head=16)
+
+
 @pytest.mark.parametrize("Hq,Hkv,d,causal", [(4, 2, 128, True), (2, 2, 64, False), (2, 1, 256, True)])
 def test_fwd_bf16_long_sequence_16384(Hq, Hkv, d, causal):
     # 64 (causal: 1 to 256) key tiles per query tile: sampled rows against the oracle

@@ -14,9 +14,11 @@
 //     waves per SIMD; each wave owns 32 consecutive query rows and never
 //     exchanges partial results with another wave (head dim 256: 128-row
 //     tiles, 16 rows per wave, so the accumulator keeps its register size);
-//   * short sequences (N <= 512, head dim <= 128): workgroups of 4 waves (128
-//     rows) with 32-key tiles, 48 KiB of LDS at head dim 128, so two
-//     workgroups share a CU and one's loads overlap the other's math;
+//   * short sequences (N <= 512), small grids (fewer than two 256-row
+//     workgroups per CU) and causal head dim 64, at head dim <= 128:
+//     workgroups of 4 waves (128 rows) with 32-key tiles, 48 KiB of LDS at
+//     head dim 128, so two (four at head dim 64) share a CU and one's loads
+//     or diagonal overlap another's math;
 //   * K/V tiles of 64 keys (32 at head dim 256) are copied global -> LDS with 16-byte direct loads
 //     into a ring of STAGES stages. The copy of tile t+STAGES-1 is issued
 //     right after the single barrier that publishes tile t+1, so it overlaps
@@ -731,11 +733,17 @@ struct FwdCfg {
   static constexpr int QPW = D == 256 ? 16 : 32, NW = 8, STAGES = 3, BN = D == 256 ? 32 : 64;
 };
 
-// Short sequences (a head's queries fill one or a few tiles, little work per
-// byte): 4-wave workgroups of 128 rows with 32-key tiles and registers kept
-// within 256 per wave, so two workgroups share a CU and one's loads overlap
-// the other's math.
+// 4-wave workgroups of 128 rows with 32-key tiles and registers kept within
+// 256 per wave, so two workgroups share a CU (four at head dim 64), for the
+// shapes where the 256-row workgroups leave the compute units waiting:
+//   * short sequences (a head's queries fill one or two tiles, little work
+//     per byte): one workgroup's loads overlap another's math;
+//   * grids of fewer than two 256-row workgroups per compute unit: twice as
+//     many workgroups;
+//   * causal at head dim 64: four resident workgroups cover the waves that
+//     stop early at the diagonal.
 constexpr int kShortSeqMaxN = 512;
+constexpr long long kFullGridWorkgroups = 2 * 256;  // two per compute unit on the 256 CUs of gfx950
 struct FwdShortCfg {
   static constexpr int QPW = 32, NW = 4, STAGES = 3, BN = 32;
 };
@@ -754,7 +762,9 @@ static hipError_t launch_fwd_bf16_short(const FwdParams& p_in, hipStream_t strea
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_cfg(const FwdParams& p_in, hipStream_t stream) {
   if constexpr (D <= 128) {
-    if (p_in.N <= kShortSeqMaxN) return launch_fwd_bf16_short<D, CAUSAL>(p_in, stream);
+    const long long wg_full = (long long)((p_in.N + 255) / 256) * p_in.B * p_in.Hq;  // 256-row workgroups
+    if (p_in.N <= kShortSeqMaxN || wg_full < kFullGridWorkgroups || (D == 64 && CAUSAL))
+      return launch_fwd_bf16_short<D, CAUSAL>(p_in, stream);
   }
   using C = FwdCfg<D>;
   FwdParams p = p_in;
