@@ -165,7 +165,9 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, contents ignored on entry (float32 scratch for the row
  * term, stored negated as -D_i = -sum_c dout_ic o_ic, and for lse_i * log2 e,
- * both written by the first kernel for the second). All three outputs are bitwise repeatable
+ * both written by the first kernel for the second; and, for grouped heads on
+ * grids too small to reach every compute unit, float32 partial dK, dV sums
+ * over parts of each K/V head's query heads, added up by a third kernel). All three outputs are bitwise repeatable
  * (no atomics). Supported d: 64, 128, 256. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -177,8 +179,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * results, plus `events`, an array of 3 hipEvent_t created by the caller (or
  * NULL, then this is exactly fa_bwd). The events are recorded on `stream`
  * before the dQ kernel (which also computes the row term D), between it and
- * the dK/dV kernel, and after the dK/dV kernel, so that each of the two
- * kernels can be timed on its own. */
+ * the dK/dV kernel, and after the dK/dV kernel (and the reduction of split
+ * head groups, when there is one), so that each of the two stages can be
+ * timed on its own. */
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,

@@ -123,6 +123,24 @@ def test_bwd_d256_causal_4096():
     assert np.abs(dk.sum(axis=2)).max() <= 2e-2 * np.abs(dk).max() * 64
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,causal,hk", [(1, 16, 2, 1024, True, 1), (4, 16, 4, 2048, False, 2)])
+def test_bwd_gqa_group_parts(B, Hq, Hkv, N, causal, hk):
+    # B1 Hq16 Hkv2 N1024: 16 dK/dV workgroups, so the 8 query heads of each K/V head are split into 8 parts whose
+    # fp32 partial sums a reduction adds up; B4 Hq16 Hkv4: 256 workgroups, no split. One K/V group in full.
+    _say(f"bwd GQA B{B} Hq{Hq} Hkv{Hkv} N{N} d128 causal={causal}: group {hk} of batch {B - 1} in full")
+    inp = make_inputs(B, Hq, Hkv, N, 128, "bf16", seed=N + Hq + B, backward=True)
+    scale = 128 ** -0.5
+    dq, dk, dv = (to_f64(t) for t in _run(inp, causal, scale))
+    G, b = Hq // Hkv, B - 1
+    sl = {n: inp[n][b:b + 1, hk * G:(hk + 1) * G] for n in ("q", "dO")}
+    sl.update({n: inp[n][b:b + 1, hk:hk + 1] for n in ("k", "v")})
+    ref = attention_bwd(sl["q"], sl["k"], sl["v"], sl["dO"], causal, scale)
+    _check_grads((dq[b:b + 1, hk * G:(hk + 1) * G], dk[b:b + 1, hk:hk + 1], dv[b:b + 1, hk:hk + 1]), ref,
+                 f"group ({b},{hk})")
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all()
+
+
 def test_bwd_gqa_medium():
     _say("bwd GQA B1 Hq8 Hkv2 N777 d128 causal")
     inp = make_inputs(1, 8, 2, 777, 128, "bf16", seed=31, backward=True)

@@ -114,9 +114,27 @@ size_t splitkv_workspace(int B, int Hq, int N, int d, int n_splits) {
 
 // per query row: D_i, then (256-byte aligned) lse_i * log2(e)
 size_t bwd_row_bytes(int B, int Hq, int N) { return ((size_t)B * Hq * N * sizeof(float) + 255) & ~(size_t)255; }
-size_t bwd_workspace(int B, int Hq, int N, int d) {
-  (void)d;
-  return 2 * bwd_row_bytes(B, Hq, N);
+
+// Parts the query heads of each K/V head's group are split into for the dK/dV
+// kernel: enough for its grid of (key tile, batch * K/V head) workgroups to
+// reach every compute unit, at most one per query head (1: no split). Each
+// part writes fp32 partial dK, dV sums, added up by a reduction kernel.
+int bwd_group_splits(int B, int Hq, int Hkv, int N, int d) {
+  const int G = Hq / Hkv;
+  if (G <= 1) return 1;
+  const int bnk = d == 256 ? 64 : 128;  // keys per dK/dV workgroup
+  const long long n_wg = (long long)((N + bnk - 1) / bnk) * B * Hkv;
+  if (n_wg >= kComputeUnits) return 1;
+  return (int)std::min<long long>(G, (kComputeUnits + n_wg - 1) / n_wg);
+}
+// split dK/dV partial sums: dV^T parts then dK^T parts, [2][S][B * Hkv][N][d] fp32
+size_t bwd_part_bytes(int B, int Hq, int Hkv, int N, int d) {
+  const int S = bwd_group_splits(B, Hq, Hkv, N, d);
+  if (S <= 1) return 0;
+  return ((size_t)2 * S * B * Hkv * N * (size_t)d * sizeof(float) + 255) & ~(size_t)255;
+}
+size_t bwd_workspace(int B, int Hq, int Hkv, int N, int d) {
+  return 2 * bwd_row_bytes(B, Hq, N) + bwd_part_bytes(B, Hq, Hkv, N, d);
 }
 
 }  // namespace
@@ -246,7 +264,7 @@ int fa_fwd_fp8(const unsigned char* q_codes, const unsigned char* k_codes, const
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shapes(B, Hq, Hkv, N, d, 0, 1.0f, true) != FA_OK) return 0;
-  return bwd_workspace(B, Hq, N, d);
+  return bwd_workspace(B, Hq, Hkv, N, d);
 }
 
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -257,7 +275,7 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   if (B == 0 || N == 0) return FA_OK;
   st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace});
   if (st != FA_OK) return st;
-  if (workspace_bytes < bwd_workspace(B, Hq, N, d)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < bwd_workspace(B, Hq, Hkv, N, d)) return FA_ERR_INVALID_ARG;
   if (events != nullptr) {
     for (int i = 0; i < 3; ++i)
       if (events[i] == nullptr) return FA_ERR_INVALID_ARG;
@@ -277,6 +295,8 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   const size_t rows = (size_t)B * Hq * N;
   p.delta = (float*)workspace;
   p.lse2 = (float*)((char*)workspace + bwd_row_bytes(B, Hq, N));
+  p.n_gsplit = bwd_group_splits(B, Hq, Hkv, N, d);
+  p.dkv_part = p.n_gsplit > 1 ? (float*)((char*)workspace + 2 * bwd_row_bytes(B, Hq, N)) : nullptr;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

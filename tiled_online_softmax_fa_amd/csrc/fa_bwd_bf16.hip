@@ -85,7 +85,11 @@ struct DualSwizzle {
 // stream through a 3-stage ring of asynchronous copies: at step s tile s is
 // read by A, tile s-1 by B, and the stage of tile s-2 receives tile s+1.
 // For grouped heads the sequence of tiles covers every query head of the
-// group, so dK and dV are summed in registers.
+// group, so dK and dV are summed in registers; when the grid of (key tile,
+// batch * K/V head) workgroups is too small to reach every compute unit, the
+// group's query heads are split into p.n_gsplit parts (blockIdx.x / grid),
+// each part writes its fp32 partial sums, and fa_bwd_dkdv_reduce_kernel adds
+// them up.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
@@ -117,7 +121,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int g = lane >> 4, L = lane & 15;
   const int G = p.Hq / p.Hkv;
 
-  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
+  const int n_wg = p.n_tiles * p.B * p.Hkv;  // workgroups per part of the head group
+  const int part = (int)blockIdx.x / n_wg;
+  const TileCoord tc = map_workgroup((int)blockIdx.x - part * n_wg, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
+  const int g_lo = part * G / p.n_gsplit;                     // this part's query heads of the group
+  const int n_heads = (part + 1) * G / p.n_gsplit - g_lo;
   const int b = tc.head / p.Hkv;
   const int hk = tc.head - b * p.Hkv;
   const int kv0 = tc.tile * BNK;
@@ -127,14 +135,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int nq = (N + BMQ - 1) / BMQ;
   const int t_first = CAUSAL ? kv0 / BMQ : 0;  // first query tile with a visible key
   const int per_head = nq - t_first;
-  const int n_seq = per_head * G;             // tiles in the sequence (all heads of the group)
+  const int n_seq = per_head * n_heads;       // tiles in the sequence (this part's heads of the group)
 
-  // ---- copies of sequence tile j (query head hk*G + j / per_head, query tile
-  // t_first + j % per_head) into stage j % STAGES
+  // ---- copies of sequence tile j (query head hk*G + g_lo + j / per_head,
+  // query tile t_first + j % per_head) into stage j % STAGES
   auto issue_tile_copy = [&](int j) __attribute__((always_inline)) {
     const int gi = j / per_head;
     const int tq = t_first + (j - gi * per_head);
-    const size_t qh = (size_t)(b * p.Hq + hk * G + gi) * N;
+    const size_t qh = (size_t)(b * p.Hq + hk * G + g_lo + gi) * N;
     const uint32_t dst = lds_address(smem) + (j % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int c = 0; c < PIECES_PER_WAVE; ++c) {
@@ -326,7 +334,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int t_clean0 = CAUSAL ? t_first + (BNK + BMQ - 2) / BMQ : 0;  // first tile no wave of the workgroup masks
     const int t_clean1 = N / BMQ;                                        // end of the full tiles
     int s = 0;
-    for (int gi = 0; gi < G; ++gi) {
+    for (int gi = 0; gi < n_heads; ++gi) {
       int tq = t_first;
       for (; tq < min(t_clean0, nq); ++tq, ++s) {
         begin_step(s);
@@ -357,6 +365,18 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   // ---- dV = dV^T acc (wave A), dK = scale * dK^T acc (wave B); lane: key
   // column, rows d = 16 db + 4 g + r
+  if (p.n_gsplit > 1) {  // this part's fp32 sums, unscaled
+    float* part_out = p.dkv_part + ((size_t)(role * p.n_gsplit + part) * p.B * p.Hkv * N + kv_head) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = kw0 + kb * 16 + L;
+      if (key < N) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *(f32x4*)(part_out + (size_t)key * D + db * 16 + 4 * g) = acc[db][kb];
+      }
+    }
+    return;
+  }
   __bf16* out = (__bf16*)(role == 0 ? p.dv : p.dk) + kv_head * D;
   const float osc = role == 0 ? 1.0f : p.scale;
 #pragma unroll
@@ -372,6 +392,25 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// Split head groups: dV = sum of the parts' dV^T, dK = scale * sum of the
+// parts' dK^T, per key row (rows = B * Hkv * N), D / 4 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_dkdv_reduce_kernel(BwdParams p, long long rows) {
+  constexpr int LPR = D / 4;  // lanes per row
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c4 = threadIdx.x % LPR;
+  if (row >= rows) return;
+  const int S = p.n_gsplit;
+  f32x4 sv = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    sv += *(const f32x4*)(p.dkv_part + ((size_t)s * rows + row) * D + c4 * 4);
+    sk += *(const f32x4*)(p.dkv_part + ((size_t)(S + s) * rows + row) * D + c4 * 4);
+  }
+  sk *= p.scale;
+  *(u32x2*)((__bf16*)p.dv + row * D + c4 * 4) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+  *(u32x2*)((__bf16*)p.dk + row * D + c4 * 4) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+}
+
 // ------------------------------------------------------------------ kernel 1: dQ (and D)
 //
 // One workgroup of 8 waves per (query tile of 256 rows, 128 at d = 256,
@@ -384,10 +423,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 // dQ = scale * dQ^T at the end. K/V tiles of 64 keys (32 at d = 256) stream
 // through a ring of STAGES stages with asynchronous direct copies, one
 // barrier per tile.
-template <int D, bool CAUSAL, int STAGES = 3>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
+// NW, BN: 8 waves (256-row query tiles) with 64-key tiles, or, for short
+// sequences and small grids, 4 waves (128 rows) with 32-key tiles, 48 KiB of
+// LDS at head dim 128, so that two workgroups share a compute unit.
+template <int D, bool CAUSAL, int STAGES = 3, int NW = 8, int BN = (D == 256 ? 32 : 64)>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int QPW = D == 256 ? 16 : 32, NW = 8, BM = QPW * NW, BN = D == 256 ? 32 : 64;
+  constexpr int QPW = D == 256 ? 16 : 32, BM = QPW * NW;
   constexpr int QB = QPW / 16, DC = D / 32, DB = D / 16, CPT = BN / 32;
   constexpr int RB = 2 * D;  // bytes per tile row
   constexpr int TILE_BYTES = BN * RB;
@@ -615,14 +657,32 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
   hipError_t e;
   // dQ first: it also writes -D (the row term, negated) that the dK/dV kernel reads
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  p.n_tiles = (p.N + BM_DQ - 1) / BM_DQ;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream, p);
+  bool small = false;  // short sequences or fewer than two 256-row workgroups per compute unit
+  if constexpr (D <= 128) small = p.N <= 512 || (long long)((p.N + BM_DQ - 1) / BM_DQ) * p.B * p.Hq < 2 * 256;
+  if (small) {
+    if constexpr (D <= 128) {
+      p.n_tiles = (p.N + 127) / 128;
+      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 3, 4, 32>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(256),
+                         0, stream, p);
+    }
+  } else {
+    p.n_tiles = (p.N + BM_DQ - 1) / BM_DQ;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hq)), dim3(512), 0, stream,
+                       p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   p.n_tiles = (p.N + BN_DKDV - 1) / BN_DKDV;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv)), dim3(512), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(p.n_tiles * p.B * p.Hkv * p.n_gsplit)), dim3(512),
+                     0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.n_gsplit > 1) {
+    const long long rows = (long long)p.B * p.Hkv * p.N;
+    const long long rows_per_block = 256 / (D / 4);
+    hipLaunchKernelGGL((fa_bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                       dim3(256), 0, stream, p, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
