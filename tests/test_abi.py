@@ -80,6 +80,12 @@ def test_backward_argument_errors():
     assert ws >= 2 * 8 * 4
     assert lib.fa_bwd_workspace_bytes(1, 2, 2, 8, 96) == 0
     assert lib.fa_bwd_workspace_bytes(1, 3, 2, 8, 64) == 0
+    # empty problems: a size (nothing is launched), for grouped and ungrouped heads
+    for shape in ((0, 2, 2, 8, 64), (1, 2, 2, 0, 64), (0, 8, 2, 16, 128), (1, 8, 2, 0, 256)):
+        lib.fa_bwd_workspace_bytes(*shape)
+    # small grids split the dK/dV work: the workspace also holds the fp32 partial sums
+    assert lib.fa_bwd_workspace_bytes(1, 4, 4, 4096, 128) >= 2 * 2 * 4 * 4096 * 128 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 16, 16, 4096, 128) < 2 * 16 * 4096 * 128
 
     def call(ptrs=None, wsb=ws, **kw):
         a = dict(B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125)

@@ -115,17 +115,20 @@ size_t splitkv_workspace(int B, int Hq, int N, int d, int n_splits) {
 // per query row: D_i, then (256-byte aligned) lse_i * log2(e)
 size_t bwd_row_bytes(int B, int Hq, int N) { return ((size_t)B * Hq * N * sizeof(float) + 255) & ~(size_t)255; }
 
-// Parts the query heads of each K/V head's group are split into for the dK/dV
-// kernel: enough for its grid of (key tile, batch * K/V head) workgroups to
-// reach every compute unit, at most one per query head (1: no split). Each
-// part writes fp32 partial dK, dV sums, added up by a reduction kernel.
+// Parts the (query head, query tile) steps of each dK/dV workgroup are split
+// into: enough for its grid of (key tile, batch * K/V head) workgroups to
+// reach every compute unit (1: no split), with about 4 steps per part or more
+// on the longest sequence, and at most kMaxDkdvParts. Each part writes fp32
+// partial dK, dV sums, added up by a reduction kernel.
+constexpr int kMaxDkdvParts = 16;
 int bwd_group_splits(int B, int Hq, int Hkv, int N, int d) {
-  const int G = Hq / Hkv;
-  if (G <= 1) return 1;
-  const int bnk = d == 256 ? 64 : 128;  // keys per dK/dV workgroup
+  const int bnk = d == 256 ? 64 : 128, bmq = d == 256 ? 32 : 64;  // keys per workgroup, query rows per step
   const long long n_wg = (long long)((N + bnk - 1) / bnk) * B * Hkv;
-  if (n_wg >= kComputeUnits) return 1;
-  return (int)std::min<long long>(G, (kComputeUnits + n_wg - 1) / n_wg);
+  if (n_wg == 0 || n_wg >= kComputeUnits) return 1;  // (empty problems launch nothing)
+  const long long steps = (long long)((N + bmq - 1) / bmq) * (Hq / Hkv);  // key tile 0: every query tile
+  long long s = (kComputeUnits + n_wg - 1) / n_wg;
+  s = std::min<long long>(s, std::max<long long>(1, steps / 4));
+  return (int)std::min<long long>(s, kMaxDkdvParts);
 }
 // split dK/dV partial sums: dV^T parts then dK^T parts, [2][S][B * Hkv][N][d] fp32
 size_t bwd_part_bytes(int B, int Hq, int Hkv, int N, int d) {

@@ -85,11 +85,11 @@ struct DualSwizzle {
 // stream through a 3-stage ring of asynchronous copies: at step s tile s is
 // read by A, tile s-1 by B, and the stage of tile s-2 receives tile s+1.
 // For grouped heads the sequence of tiles covers every query head of the
-// group, so dK and dV are summed in registers; when the grid of (key tile,
+// group, so dK and dV are summed in registers. When the grid of (key tile,
 // batch * K/V head) workgroups is too small to reach every compute unit, the
-// group's query heads are split into p.n_gsplit parts (blockIdx.x / grid),
-// each part writes its fp32 partial sums, and fa_bwd_dkdv_reduce_kernel adds
-// them up.
+// sequence of (query head, query tile) steps is split into p.n_gsplit
+// contiguous parts (part = blockIdx.x / grid), each part writes its fp32
+// partial sums, and fa_bwd_dkdv_reduce_kernel adds them up.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
@@ -124,8 +124,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int n_wg = p.n_tiles * p.B * p.Hkv;  // workgroups per part of the head group
   const int part = (int)blockIdx.x / n_wg;
   const TileCoord tc = map_workgroup((int)blockIdx.x - part * n_wg, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
-  const int g_lo = part * G / p.n_gsplit;                     // this part's query heads of the group
-  const int n_heads = (part + 1) * G / p.n_gsplit - g_lo;
   const int b = tc.head / p.Hkv;
   const int hk = tc.head - b * p.Hkv;
   const int kv0 = tc.tile * BNK;
@@ -135,15 +133,18 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int nq = (N + BMQ - 1) / BMQ;
   const int t_first = CAUSAL ? kv0 / BMQ : 0;  // first query tile with a visible key
   const int per_head = nq - t_first;
-  const int n_seq = per_head * n_heads;       // tiles in the sequence (this part's heads of the group)
+  const int n_all = per_head * G;             // steps of the whole sequence (all heads of the group)
+  const int j0 = (int)((long long)part * n_all / p.n_gsplit);  // this part's steps: j0 .. j0 + n_seq - 1
+  const int n_seq = (int)((long long)(part + 1) * n_all / p.n_gsplit) - j0;
 
-  // ---- copies of sequence tile j (query head hk*G + g_lo + j / per_head,
-  // query tile t_first + j % per_head) into stage j % STAGES
-  auto issue_tile_copy = [&](int j) __attribute__((always_inline)) {
+  // ---- copies of step jl of this part (sequence step j = j0 + jl: query head
+  // hk*G + j / per_head, query tile t_first + j % per_head) into stage jl % STAGES
+  auto issue_tile_copy = [&](int jl) __attribute__((always_inline)) {
+    const int j = j0 + jl;
     const int gi = j / per_head;
     const int tq = t_first + (j - gi * per_head);
-    const size_t qh = (size_t)(b * p.Hq + hk * G + g_lo + gi) * N;
-    const uint32_t dst = lds_address(smem) + (j % STAGES) * STAGE_BYTES;
+    const size_t qh = (size_t)(b * p.Hq + hk * G + gi) * N;
+    const uint32_t dst = lds_address(smem) + (jl % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int c = 0; c < PIECES_PER_WAVE; ++c) {
       const int piece = wave * PIECES_PER_WAVE + c;
@@ -334,19 +335,22 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int t_clean0 = CAUSAL ? t_first + (BNK + BMQ - 2) / BMQ : 0;  // first tile no wave of the workgroup masks
     const int t_clean1 = N / BMQ;                                        // end of the full tiles
     int s = 0;
-    for (int gi = 0; gi < n_heads; ++gi) {
-      int tq = t_first;
-      for (; tq < min(t_clean0, nq); ++tq, ++s) {
+    while (s < n_seq) {  // one query head's run of this part's steps
+      const int j = j0 + s;
+      const int gi = j / per_head;
+      const int tq_end = t_first + min(per_head, j0 + n_seq - gi * per_head);
+      int tq = t_first + (j - gi * per_head);
+      for (; tq < min(t_clean0, tq_end); ++tq, ++s) {
         begin_step(s);
 #pragma unroll
         for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::true_type{});
       }
-      for (; tq < t_clean1; ++tq, ++s) {
+      for (; tq < min(t_clean1, tq_end); ++tq, ++s) {
         begin_step(s);
 #pragma unroll
         for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::false_type{});
       }
-      for (; tq < nq; ++tq, ++s) {
+      for (; tq < tq_end; ++tq, ++s) {
         begin_step(s);
 #pragma unroll
         for (int cc = 0; cc < CPQ; ++cc) chunk_a(stage_of(s), tq * BMQ, cc, pbuf_of(s), std::true_type{});

@@ -43,7 +43,7 @@ struct BwdParams {
   void* dv;
   float* delta;   // [B, Hq, N] workspace: -D_i = -sum_c dout_ic o_ic (the dP accumulators start there)
   float* lse2;    // [B, Hq, N] workspace: lse_i * log2(e), written with D by the dQ kernel
-  int n_gsplit;     // parts of each K/V head's query-head group in the dK/dV kernel (1: none)
+  int n_gsplit;     // parts of each dK/dV workgroup's (query head, query tile) sequence (1: none)
   float* dkv_part;  // n_gsplit > 1: [2][n_gsplit][B * Hkv][N][d] fp32 partial dV^T, dK^T sums (dK unscaled)
   int B, Hq, Hkv, N;
   float scale;
