@@ -34,28 +34,29 @@ namespace fa {
 
 // ------------------------------------------------------------------ LDS layout shared by both kernels
 //
-// Tiles here are read both row-wise (16-byte reads of one row's chunk) and
-// transposed (ds_read_b64_tr_b16), so the 16-byte chunk c of row r is stored
-// at chunk c ^ f(r). Over one 256-byte bank sweep, f must send the 16 rows of
-// a row-wise read (16 lanes per cycle, one chunk each) to 16 distinct
-// 16-byte slots, and the rows 0..7 (8..15) of a transposed read (32 lanes per
-// cycle, rows 4g..4g+3 of two lane groups, 32 bytes per row, i.e. two
-// adjacent chunks whose pair index is c/2 ^ f(r)/2) to 8 distinct 32-byte
-// slots. With one row per sweep (d >= 128) f(r) = (r mod 8) * 2 + bit 3 of r
-// does both; with two 128-byte rows per sweep (d = 64) the same on r / 2,
-// since the row's half of the sweep is already fixed by r mod 2. f < 16 only
-// permutes chunks inside one 256-byte bank sweep, so with 512-byte rows
-// (d = 256) chunk c + 16 sits 256 bytes after chunk c: the fragment offsets of
-// the second half of a row are those of the first plus 256 (kHalfRow below),
-// a constant. f repeats every 16 rows, as the fragment reads add whole
-// 16-row blocks.
+// Tiles here are read both row-wise (16-byte reads of one row's chunk, by the
+// 16 lanes of a lane group: rows 0..15) and transposed (ds_read_b64_tr_b16:
+// rows 4g..4g+3 of lane group g, 32 bytes per row), so the 16-byte chunk c
+// of row r is stored at chunk c ^ f(r). Measured on gfx950 (LDS bank-conflict
+// counter over masks that satisfy one rule or the other): the 16-byte reads
+// are served 8 lanes at a time from 128 bytes, the transposing reads 32 lanes
+// at a time from 256 bytes. So over any 8 consecutive rows, bits 0-2 of f
+// must differ (row-wise: 8 chunks in distinct 16-byte slots of 128 bytes) and
+// bits 1-3 must differ (transposed: 8 rows of two adjacent chunks, pair index
+// c/2 ^ f(r)/2, in distinct 32-byte slots of 256 bytes).
+// f(r) = (r mod 8) + 8 (r mod 2) does both; at d = 64 (8 chunks per
+// 128-byte row, two rows per 256 bytes, so the row's half is fixed by
+// r mod 2) f(r) = r mod 8 does. f < 16 only permutes chunks inside one
+// 256-byte sweep, so with 512-byte rows (d = 256) chunk c + 16 sits 256 bytes
+// after chunk c: the fragment offsets of the second half of a row are those of
+// the first plus 256 (r_half, t_half below), a constant. f repeats every 8 rows, as
+// the fragment reads add whole 16-row blocks.
 template <int D>
 struct DualSwizzle {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = kRowBytes / 16;
   __device__ static __forceinline__ int f(int row) {
-    const int r = kChunks >= 16 ? row : row >> 1;
-    return kChunks >= 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+    return kChunks >= 16 ? ((row & 7) | ((row & 1) << 3)) : (row & 7);
   }
   // lane offsets kept per 32-column step (row-wise reads) and per 16-column
   // block (transposed reads) within one 256-byte half row
