@@ -295,7 +295,6 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  const size_t rows = (size_t)B * Hq * N;
   p.delta = (float*)workspace;
   p.lse2 = (float*)((char*)workspace + bwd_row_bytes(B, Hq, N));
   p.n_gsplit = bwd_group_splits(B, Hq, Hkv, N, d);

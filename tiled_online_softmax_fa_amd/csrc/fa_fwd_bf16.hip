@@ -516,10 +516,6 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   // scores of a seen chunk. Both live: the straight-line step of the dense
   // loop (masked only where the diagonal or the end of the sequence cuts
   // the next chunk); otherwise only the half that exists.
-  auto chunk_needs_mask = [&](int ch) __attribute__((always_inline)) {
-    const int key_last = ch * 32 + 31;
-    return (CAUSAL && key_last > qw0) || key_last >= N;
-  };
   auto chunk_seen = [&](int ch, bool block_seen) __attribute__((always_inline)) {
     return block_seen && ch * 32 < N && !(CAUSAL && ch * 32 > qw0 + QPW - 1);
   };
