@@ -31,11 +31,24 @@ def _say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,seed", _cases(16, 2026))
-def test_sweep_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
+def _small_grid_cases(n, seed):
+    """Shapes whose grids are smaller than the GPU: the forward and dQ run 128-row workgroups and the dK/dV
+    steps are split into parts added up by the reduction kernel."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 4]))
+        N = int(rng.integers(200, 1200))
+        causal = bool(rng.integers(0, 2))
+        out.append((1, Hkv * G, Hkv, N, d, causal, 3000 + i))
+    return out
+
+
+def _check_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
     import tiled_online_softmax_fa_amd as fa
 
-    _say(f"sweep B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
     inp = make_inputs(B, Hq, Hkv, N, d, "bf16", seed=seed, backward=True)
     scale = d ** -0.5
     q, k, v, dO = (to_device(inp, n, "bf16") for n in ("q", "k", "v", "dO"))
@@ -55,3 +68,15 @@ def test_sweep_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
             assert np.all(np.abs(g) <= bound), name
         else:
             assert_bf16_close(g, rf, name, scale=s)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,seed", _cases(16, 2026))
+def test_sweep_fwd_bwd(B, Hq, Hkv, N, d, causal, seed):
+    _say(f"sweep B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    _check_fwd_bwd(B, Hq, Hkv, N, d, causal, seed)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,seed", _small_grid_cases(10, 2027))
+def test_sweep_small_grids(B, Hq, Hkv, N, d, causal, seed):
+    _say(f"small-grid sweep B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}")
+    _check_fwd_bwd(B, Hq, Hkv, N, d, causal, seed)
