@@ -94,8 +94,10 @@ struct KVSwizzle {
 
 // Tuning knobs (instantiated by the launcher): QPW query rows per wave, NW
 // waves per workgroup, STAGES K/V tiles in the LDS ring. The register budget
-// follows from NW waves per CU: 8 waves put two on every SIMD, and the vector
-// phase of one overlaps the matrix phase of the other. PRIO raises the
+// follows from the waves per CU: 8 waves (one workgroup) put two on every
+// SIMD, and the vector phase of one overlaps the matrix phase of the other;
+// 4-wave workgroups are held to 256 registers per wave so that two of them
+// share a CU (waves_per_eu(2)). PRIO raises the
 // wave's issue priority around its runs of matrix instructions, so the wave
 // that has MFMA work ready wins the issue slot and the other wave's vector
 // work fills the gaps.
