@@ -662,8 +662,11 @@ static hipError_t launch_bwd_cfg(const BwdParams& p_in, hipStream_t stream, hipE
   hipError_t e;
   // dQ first: it also writes -D (the row term, negated) that the dK/dV kernel reads
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  bool small = false;  // short sequences or fewer than two 256-row workgroups per compute unit
-  if constexpr (D <= 128) small = p.N <= 512 || (long long)((p.N + BM_DQ - 1) / BM_DQ) * p.B * p.Hq < 2 * 256;
+  // short sequences, fewer than two 256-row workgroups per compute unit, or
+  // causal at head dim 64 (four 128-row workgroups per compute unit)
+  bool small = false;
+  if constexpr (D <= 128)
+    small = p.N <= 512 || (long long)((p.N + BM_DQ - 1) / BM_DQ) * p.B * p.Hq < 2 * 256 || (D == 64 && CAUSAL);
   if (small) {
     if constexpr (D <= 128) {
       p.n_tiles = (p.N + 127) / 128;
