@@ -382,19 +382,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
     return;
   }
+  // whole rows through each wave's region of the now idle LDS
+  static_assert(8 * staged_rows_bytes<D>(KPW) <= STAGES * STAGE_BYTES, "dK/dV staging must fit in the ring");
+  wait_vmcnt0();
+  __syncthreads();  // every wave is done with the ring and the P buffers
   __bf16* out = (__bf16*)(role == 0 ? p.dv : p.dk) + kv_head * D;
-  const float osc = role == 0 ? 1.0f : p.scale;
+  float osc[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw0 + kb * 16 + L;
-    if (key < N) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 v4 = acc[db][kb] * osc;
-        *(u32x2*)(out + (size_t)key * D + db * 16 + 4 * g) = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-      }
-    }
-  }
+  for (int kb = 0; kb < KB; ++kb) osc[kb] = role == 0 ? 1.0f : p.scale;
+  store_rows_through_lds<D, KB>(smem + wave * staged_rows_bytes<D>(KPW), acc, osc, out, kw0, N, lane);
 }
 
 // Split head groups: dV = sum of the parts' dV^T, dK = scale * sum of the
@@ -638,20 +634,15 @@ void fa_bwd_dq_kernel(BwdParams p) {
       if (CPT * t + cc < n_ch) chunk(kt + cc * 32 * RB, CPT * t + cc, std::true_type{});
   }
 
-  // dQ = scale * dQ^T: lane holds query L + 16 qb, d = 16 db + 4 g + r
-  __bf16* dqg = (__bf16*)p.dq + qh * D;
+  // dQ = scale * dQ^T: lane holds query L + 16 qb, d = 16 db + 4 g + r;
+  // whole rows through each wave's region of the now idle K/V ring
+  static_assert(NW * staged_rows_bytes<D>(QPW) <= STAGES * 2 * TILE_BYTES, "dQ staging must fit in the ring");
+  wait_vmcnt0();
+  __syncthreads();  // every wave is done with the K/V ring
+  float sc[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 16 + L;
-    if (row < N) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 v4 = acc[db][qb] * p.scale;
-        *(u32x2*)(dqg + (size_t)row * D + db * 16 + 4 * g) =
-            u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-      }
-    }
-  }
+  for (int qb = 0; qb < QB; ++qb) sc[qb] = p.scale;
+  store_rows_through_lds<D, QB>(smem + wave * staged_rows_bytes<D>(QPW), acc, sc, (__bf16*)p.dq + qh * D, qw0, N, lane);
 }
 
 // ------------------------------------------------------------------ launch

@@ -168,4 +168,41 @@ __device__ __forceinline__ TileCoord map_workgroup(int wg, int n_heads, int n_ti
   return TileCoord{head, heavy_first ? (n_tiles - 1 - rank) : rank};
 }
 
+// Stores a wave's results as whole bf16 rows. An accumulator acc[db][rb]
+// holds, in lane (L = lane & 15, g = lane >> 4), row 16 rb + L, columns
+// 16 db + 4 g .. 16 db + 4 g + 3, times mul[rb]; stored directly, every
+// instruction would write 16 rows in 32-byte pieces. The rows go through
+// `region` (16 NRB rows of 2 D + 16 bytes owned by this wave; the padding
+// spreads the 16 rows of a block over the LDS banks for the 8-byte writes)
+// and leave 16 bytes per lane, so that an instruction writes 64 x 16 bytes of
+// consecutive rows, in whole cache lines. Row r goes to out + (row0 + r) D
+// when row0 + r < n_rows. The wave reads back only what it wrote itself, and
+// its LDS operations complete in order.
+template <int D, int NRB>
+__device__ __forceinline__ void store_rows_through_lds(lds_u8* region, const f32x4 (&acc)[D / 16][NRB],
+                                                       const float (&mul)[NRB], __bf16* out, int row0, int n_rows,
+                                                       int lane) {
+  constexpr int RS = 2 * D + 16;   // bytes per staged row
+  constexpr int LPR = 2 * D / 16;  // lanes per row when storing
+  constexpr int RPI = 64 / LPR;    // rows per store instruction
+  const int g = lane >> 4, L = lane & 15;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const f32x4 v = acc[db][rb] * mul[rb];
+      *(FA_LDS u32x2*)(region + (rb * 16 + L) * RS + (db * 16 + g * 4) * 2) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+#pragma unroll
+  for (int r0 = 0; r0 < NRB * 16; r0 += RPI) {
+    const int r = r0 + lane / LPR;
+    const u32x4 v = *(const FA_LDS u32x4*)(region + r * RS + (lane % LPR) * 16);
+    if (row0 + r < n_rows) *(u32x4*)((char*)(out + (size_t)(row0 + r) * D) + (lane % LPR) * 16) = v;
+  }
+}
+// LDS bytes store_rows_through_lds stages for `rows` rows
+template <int D>
+constexpr int staged_rows_bytes(int rows) { return rows * (2 * D + 16); }
+
 }  // namespace fa

@@ -680,43 +680,22 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       }
     }
   } else {
-    // O leaves through LDS. A lane holds 4 consecutive columns of a row per
-    // accumulator block, so stored directly every instruction would write 16
-    // rows in 32-byte pieces; each wave instead puts its rows (bf16) into a
-    // region of its own in the now idle K/V ring and stores them back whole,
-    // 16 bytes per lane, so that one instruction writes 64 lanes x 16 bytes
-    // of consecutive rows. All workgroups finish at nearly the same time, so
-    // this final write-back of O is a burst; in full lines it drains faster.
-    // Rows are padded by 16 bytes, which spreads the 16 rows of a block over
-    // the LDS banks for the 8-byte writes.
-    constexpr int ORS = 2 * D + 16;
-    static_assert(NW * QPW * ORS <= STAGES * STAGE_BYTES, "O staging must fit in the K/V ring");
+    // O leaves as whole rows through each wave's region of the now idle K/V
+    // ring (store_rows_through_lds). All workgroups finish at nearly the
+    // same time, so this final write-back of O is a burst, which drains
+    // faster in whole cache lines.
+    static_assert(NW * staged_rows_bytes<D>(QPW) <= STAGES * STAGE_BYTES, "O staging must fit in the K/V ring");
     __syncthreads();  // every wave is done with the K/V ring (no copy is in flight)
-    lds_u8* const ow = smem + wave * (QPW * ORS);
+    float inv[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l = sum_over_row_groups(l_part[qb]);
       const int row = qw0 + qb * 16 + L;
       // (sparse: a row that saw no key has l = 0 and gets O = 0, lse = -inf)
-      const float inv = (!SPARSE || l > 0.f) ? 1.0f / l : 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 o4 = acc[db][qb] * inv;
-        *(FA_LDS u32x2*)(ow + (qb * 16 + L) * ORS + (db * 16 + g * 4) * 2) =
-            u32x2{pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3])};
-      }
+      inv[qb] = (!SPARSE || l > 0.f) ? 1.0f / l : 0.f;
       if (g == 0 && row < N) lseg[row] = (!SPARSE || l > 0.f) ? (m_ref[qb] + log2_fast(l)) * kLn2 : kNegInf;
     }
-    // (the wave reads back what it wrote itself: its LDS operations complete in order)
-    constexpr int LPR = 2 * D / 16;  // lanes per row
-    constexpr int RPI = 64 / LPR;    // rows per store instruction
-#pragma unroll
-    for (int r0 = 0; r0 < QPW; r0 += RPI) {
-      const int rr = r0 + lane / LPR;
-      const int row = qw0 + rr;
-      const u32x4 v = *(const FA_LDS u32x4*)(ow + rr * ORS + (lane % LPR) * 16);
-      if (row < N) *(u32x4*)((char*)(og + (size_t)row * D) + (lane % LPR) * 16) = v;
-    }
+    store_rows_through_lds<D, QB>(smem + wave * staged_rows_bytes<D>(QPW), acc, inv, og, qw0, N, lane);
   }
 }
 
