@@ -494,7 +494,7 @@ def main():
         return write_traffic(*args.traffic_from)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this library runs a single "
-              "MI355X; the multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+              "MI355X; sharding across GPUs is not built)", file=sys.stderr)
         return 2
 
     import numpy as np
