@@ -6,10 +6,8 @@ import numpy as np
 import pytest
 
 from fa_inputs import bf16_bits_to_f32, bf16_round_bits, make_inputs
-from fa_testlib import (assert_bf16_close, assert_lse_close, errors, lse_bound, lse_bound_rows, to_device, to_f64,
-                        torch_mod)
-from oracle import (attention_fwd, attention_fwd_fp8, attention_fwd_rows, dequantize_blockwise_e4m3,
-                    quantize_blockwise_e4m3)
+from fa_testlib import assert_bf16_close, assert_lse_close, errors, lse_bound, to_device, to_f64, torch_mod
+from oracle import attention_fwd, attention_fwd_fp8, dequantize_blockwise_e4m3, quantize_blockwise_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -119,24 +117,26 @@ def test_fwd_fp8_peaky_with_gpu_quantised_inputs():
 
 
 def test_fwd_fp8_workload_causal_4096():
-    # B2 H16 N4096 d128 causal: sampled rows of every head against the dequantised definition
+    # B2 H16 N4096 d128 causal: every element of O and lse against the dequantised definition
     B, H, N, d = 2, 16, 4096, 128
     inp, qc, qs, kc, ks = _fp8_inputs(B, H, H, N, d, seed=2)
     o, lse = _run_fp8(qc, qs, kc, ks, inp, True, d ** -0.5)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     qd = dequantize_blockwise_e4m3(qc, qs)
     kd = dequantize_blockwise_e4m3(kc, ks)
-    rng = np.random.default_rng(4)
-    worst = 0.0
+    worst, total, lworst = 0.0, 0.0, 0.0
     for b in range(B):
         for h in range(H):
-            rows = np.unique(np.concatenate([[0, 63, 64, N - 1], rng.integers(0, N, 12)]))
-            Or, Lr = attention_fwd_rows(qd, kd, inp["v"], True, d ** -0.5, b, h, rows)
-            mx = errors(o[b, h, rows], Or)[0]
-            worst = max(worst, mx)
-            assert mx <= 2e-2
-            assert_lse_close(lse[b, h, rows], Lr, lse_bound_rows(qd[b, h][rows], kd[b, h], d ** -0.5))
-    _say(f"  sampled rows worst max {worst:.2e}")
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            O, LSE = attention_fwd(qd[sl], kd[sl], inp["v"][sl], True, d ** -0.5)
+            e = np.abs(o[sl] - O)
+            worst = max(worst, float(e.max()))
+            total += float(e.sum())
+            assert worst <= 2e-2, f"head ({b},{h}): max {worst:.3e}"
+            lworst = max(lworst, assert_lse_close(lse[sl], LSE, lse_bound(qd[sl], kd[sl], d ** -0.5)))
+    mean = total / o.size
+    _say(f"  whole tensor O max {worst:.2e} mean {mean:.2e}, lse max {lworst:.2e}")
+    assert mean <= 2e-3
 
 
 def test_fwd_fp8_errors():

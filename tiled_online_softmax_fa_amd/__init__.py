@@ -341,12 +341,21 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
     goes through fa_bwd_timed, which records them around its two kernels.
     """
     torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _require(t, torch.bfloat16, n)
-    _require(lse, torch.float32, "lse")
+    # every shape first: the library sees only pointers, so an output smaller
+    # than q (dq) or k (dk, dv) would be written past its end
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        if t is not None and not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
     B, Hq, Hkv, N, d = _dims(q, k, v)
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("o/dout/lse have the wrong shape")
+    for t, n, want in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", v.shape)):
+        if t is not None and tuple(t.shape) != tuple(want):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(want)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, torch.bfloat16, n)
+    _require(lse, torch.float32, "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
