@@ -87,17 +87,27 @@ def source_digest(names=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, launches_note):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on the kernel's current sources."""
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the kernel's current sources.
+
+    Returns (bytes or None, provenance text)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    digest = source_digest(KERNEL_SOURCES[kernel_key])
     if not os.path.exists(path):
-        return None
+        return None, "no profiles/traffic.json"
     with open(path) as f:
         t = json.load(f)
     k = t.get("kernels", {}).get(kernel_key)
-    if k is None or k.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_key]):
-        return None
-    return k.get("hbm_bytes_per_launch")
+    if k is None:
+        return None, f"profiles/traffic.json has no entry for {kernel_key}"
+    if k.get("source_digest") != digest:
+        return None, (f"profiles/traffic.json was taken on sources {k.get('source_digest')}, the kernel's sources "
+                      f"are now {digest}: stale, not reported")
+    cal = t.get("calibration", {})
+    return k.get("hbm_bytes_per_launch"), (
+        f"profiles/traffic.json (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE of bench.py, two runs, KiB per dispatch "
+        f"scaled by the copy calibration x{cal.get('fetch_factor', float('nan')):.4f} / "
+        f"x{cal.get('write_factor', float('nan')):.4f}), source digest {digest} = current sources")
 
 
 PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 MFMA
@@ -438,27 +448,42 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     return 0
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (else the machine type)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(inputs, budget_s=10.0):
-    """Time the fp64 oracle (fwd + bwd per head) on a bounded sample of the same workload."""
-    from threadpoolctl import threadpool_info
+    """Time the fp64 oracle (fwd + bwd per head) on a bounded sample of the same workload, with the BLAS
+    thread pool set to the CPUs this process may run on."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import attention_bwd_head, attention_fwd
 
     w = WORKLOAD
     scale = w["d"] ** -0.5
     heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
-    t0 = time.perf_counter()
-    done = 0
-    for b, h in heads:
-        q, k, v, dO = (inputs[n][b:b + 1, h:h + 1] for n in ("q", "k", "v", "dO"))
-        attention_fwd(q, k, v, True, scale)
-        attention_bwd_head(q[0, 0], k[0, 0], v[0, 0], dO[0, 0], True, scale)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    secs = time.perf_counter() - t0
+    n_cpus = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=n_cpus, user_api="blas"):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        t0 = time.perf_counter()
+        done = 0
+        for b, h in heads:
+            q, k, v, dO = (inputs[n][b:b + 1, h:h + 1] for n in ("q", "k", "v", "dO"))
+            attention_fwd(q, k, v, True, scale)
+            attention_bwd_head(q[0, 0], k[0, 0], v[0, 0], dO[0, 0], True, scale)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        secs = time.perf_counter() - t0
     f, b_ = flops(1, done, w["N"], w["d"], True)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": (f + b_) / secs / 1e12,
         "unit": "TFLOP/s",
@@ -466,7 +491,8 @@ def cpu_baseline(inputs, budget_s=10.0):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (batch, head) pairs of the same workload, fwd + bwd each, "
                   f"fp64 NumPy with the full N x N matrix, {secs:.1f} s",
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
+        "affinity_cpus": n_cpus,
     }
 
 
@@ -583,8 +609,9 @@ def main():
         achieved, peak, unit = units / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = units / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    traffic, traffic_source = measured_traffic(dominant)
     roofline = {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": measured_traffic(dominant, "per launch"),
+                "frac": achieved / peak, "traffic": traffic, "traffic_source": traffic_source,
                 "avg_launch_us": kern_ms[dominant] * 1e3}
     kernels = {}
     for name, ms in kern_ms.items():
