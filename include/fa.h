@@ -26,7 +26,8 @@
  *            row: lse_i = log(sum_j exp(scale * q_i.k_j)).
  *  Memory    every pointer is a device pointer owned by the caller; the
  *            library never allocates, frees or keeps a pointer past the call.
- *            Base pointers must be 16-byte aligned.
+ *            Base pointers must be 16-byte aligned. (fa_bwd_noalloc keeps its
+ *            scratch in a fixed array of the library's own, one per GPU.)
  *  Streams   work is enqueued on `stream` (NULL = the default stream) and the
  *            call returns without synchronising; a device-side fault shows at
  *            the caller's next synchronisation.
@@ -36,8 +37,9 @@
  *            Argument checks run before any HIP call, so FA_ERR_INVALID_ARG and
  *            FA_ERR_UNSUPPORTED (shape) never depend on a device being present.
  *  Threads   the library keeps no state besides a per-device architecture
- *            check cached on first use; calls from several host threads are
- *            safe.
+ *            check cached on first use (and the per-device address of
+ *            fa_bwd_noalloc's scratch); calls from several host threads are
+ *            safe, except overlapping fa_bwd_noalloc calls on one GPU.
  */
 #ifndef FA_H
 #define FA_H
@@ -55,7 +57,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = -2, /* head dim not supported, or device is not gfx950 */
   FA_ERR_DEVICE = -3,      /* no usable HIP device / device query failed */
   FA_ERR_LAUNCH = -4,      /* a kernel launch reported an error */
-  FA_ERR_INTERNAL = -5
+  FA_ERR_INTERNAL = -5,
+  FA_ERR_TOO_LARGE = -6    /* the problem needs more scratch than fa_bwd_noalloc holds */
 } fa_status;
 
 /* Forward, bf16 storage (q, k, v, o as bf16 bit patterns), float32 arithmetic
@@ -187,6 +190,25 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes,
                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                  hipStream_t stream, hipEvent_t* events);
+
+/* Scratch held per GPU by fa_bwd_noalloc: 32 MiB. */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * fa_bwd with the same arguments, layouts, kernels and results (bit for bit),
+ * minus the workspace: it uses a scratch array of FA_BWD_NOALLOC_SCRATCH_BYTES
+ * that the library holds in each GPU's memory from that GPU's first call
+ * until the process ends, and it calls no hipMalloc, hipFree or allocating
+ * library routine. Problems whose fa_bwd_workspace_bytes(...) exceed it get
+ * FA_ERR_TOO_LARGE before any HIP call (about 2^22 query rows B * Hq * N
+ * without split head groups). Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (several streams or host
+ * threads) race and must be serialised by the caller. */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char* fa_status_string(int status);

@@ -25,7 +25,7 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_fwd",
                                     "fa_fwd_blocksparse", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_workspace_bytes", "fa_quantize_fp8", "fa_status_string"]
 
@@ -200,5 +200,29 @@ def test_fp8_argument_errors():
 
 def test_status_strings():
     lib = _lib()
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.fa_status_string(s)
+    assert b"scratch" in lib.fa_status_string(-6)
+
+
+def test_bwd_noalloc_argument_errors():
+    # the allocation-free backward checks sizes and its scratch limit before any HIP call
+    from tiled_online_softmax_fa_amd import (FA_ERR_INVALID_ARG as INV, FA_ERR_TOO_LARGE as BIG,
+                                             FA_ERR_UNSUPPORTED as UNS, FA_OK, BWD_NOALLOC_SCRATCH_BYTES)
+
+    lib = _lib()
+
+    def call(B=1, Hq=2, Hkv=2, N=8, d=64, causal=0, scale=0.125, ptrs=None):
+        return lib.fa_bwd_noalloc(*(ptrs or [BAD] * 9), B, Hq, Hkv, N, d, causal, scale, NULL)
+
+    assert call(d=96) == UNS
+    assert call(Hq=3, Hkv=2) == INV
+    assert call(scale=float("nan")) == INV
+    assert call(ptrs=[BAD] * 8 + [NULL]) == INV
+    assert call(N=0, ptrs=[NULL] * 9) == FA_OK
+    # B * Hq * N rows need 8 bytes of scratch each (D and lse * log2 e): 2^22 rows fit, 2^22 + 1024 do not
+    assert lib.fa_bwd_workspace_bytes(1, 1024, 1024, 4096, 128) == BWD_NOALLOC_SCRATCH_BYTES
+    assert call(B=1, Hq=1024, Hkv=1024, N=4097, d=128) == BIG
+    # grouped heads on a small grid add split dK/dV partial sums: over the limit well before 2^22 rows
+    assert lib.fa_bwd_workspace_bytes(1, 16, 1, 8192, 128) > BWD_NOALLOC_SCRATCH_BYTES
+    assert call(B=1, Hq=16, Hkv=1, N=8192, d=128) == BIG

@@ -36,6 +36,8 @@ __all__ = [
     "FP8_BLOCK",
     "bwd",
     "bwd_workspace_bytes",
+    "bwd_noalloc",
+    "BWD_NOALLOC_SCRATCH_BYTES",
     "flash_attn",
     "status_string",
     "FA_OK",
@@ -44,6 +46,7 @@ __all__ = [
     "FA_ERR_DEVICE",
     "FA_ERR_LAUNCH",
     "FA_ERR_INTERNAL",
+    "FA_ERR_TOO_LARGE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -54,6 +57,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_DEVICE = -3
 FA_ERR_LAUNCH = -4
 FA_ERR_INTERNAL = -5
+FA_ERR_TOO_LARGE = -6
 
 _lib = None
 
@@ -82,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp, vp]
     lib.fa_bwd_timed.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_splitkv.restype = i
     ll = ctypes.c_longlong
@@ -376,6 +382,34 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=No
             _check(lib.fa_bwd(*args), "fa_bwd")
         else:
             _check(lib.fa_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p)), "fa_bwd_timed")
+    return dq, dk, dv
+
+
+BWD_NOALLOC_SCRATCH_BYTES = 32 << 20  # FA_BWD_NOALLOC_SCRATCH_BYTES
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None):
+    """fa_bwd_noalloc: the backward without a workspace, for callers that cannot allocate device memory
+    (the C entry point uses the library's fixed per-GPU scratch). The outputs dq, dk, dv are caller-provided
+    bf16 tensors shaped like q, k, v; nothing is allocated here either. Calls that overlap on one GPU race.
+    Returns (dq, dk, dv)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _dims(q, k, v)
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o/dout/lse have the wrong shape")
+    for t, n, want in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", v.shape)):
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(want):
+            raise ValueError(f"{n} must be a tensor of shape {tuple(want)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _require(t, torch.bfloat16, n)
+    _require(lse, torch.float32, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    with _guard(q, k, v, o, dout, lse, dq, dk, dv):
+        st = lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream_ptr(q))
+    _check(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

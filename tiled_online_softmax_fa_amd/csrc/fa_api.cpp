@@ -315,6 +315,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                       stream, nullptr);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   hipStream_t stream) {
+  int st = check_shapes(B, Hq, Hkv, N, d, causal, scale, true);
+  if (st != FA_OK) return st;
+  if (B == 0 || N == 0) return FA_OK;
+  st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv});
+  if (st != FA_OK) return st;
+  const size_t need = bwd_workspace(B, Hq, Hkv, N, d);
+  if (need > (size_t)FA_BWD_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* scratch = nullptr;
+  if (fa::bwd_noalloc_scratch(&scratch) != hipSuccess) return FA_ERR_DEVICE;
+  return fa_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, scratch, need, B, Hq, Hkv, N, d, causal, scale, stream,
+                      nullptr);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -323,6 +341,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_DEVICE: return "no usable HIP device";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_INTERNAL: return "internal error";
+    case FA_ERR_TOO_LARGE: return "problem needs more scratch than fa_bwd_noalloc holds (FA_BWD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

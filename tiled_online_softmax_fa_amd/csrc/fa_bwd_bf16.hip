@@ -27,6 +27,9 @@
 //      "Улучшение backward pass", and blogweb.cn section 5). Two waves per
 //      32-key slice split the work: one computes P and dV, the other dP, dS
 //      and dK (details at the kernel).
+#include <mutex>
+
+#include "../../include/fa.h"
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -691,6 +694,44 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s
   if (d == 128) return causal ? launch_bwd_cfg<128, true>(p, stream, ev) : launch_bwd_cfg<128, false>(p, stream, ev);
   if (d == 64) return causal ? launch_bwd_cfg<64, true>(p, stream, ev) : launch_bwd_cfg<64, false>(p, stream, ev);
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ scratch of fa_bwd_noalloc
+//
+// The allocation-free backward keeps its workspace (the row terms and the
+// split dK/dV partial sums) in this array instead of caller memory. Every
+// GPU the library runs on holds its own copy, at its own address, until the
+// process ends. In host code the array's name stands for a host-side
+// shadow, not for device memory: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on that device's first call and cached here. Every byte a call
+// reads is first written by the same call (D and lse * log2 e by the dQ
+// kernel, each split part's sums for all of its rows), so nothing needs
+// clearing between calls; calls that overlap on one GPU share the array and
+// race.
+static __device__ __align__(256) unsigned char scratch[FA_BWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t bwd_noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

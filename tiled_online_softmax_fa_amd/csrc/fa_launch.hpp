@@ -68,5 +68,8 @@ hipError_t launch_quantize_fp8(const void* x, unsigned char* codes, float* scale
                                hipStream_t stream);
 // events: NULL or 3 events recorded before/between/after the two backward kernels
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream, hipEvent_t* events);
+// device address of this GPU's scratch array for fa_bwd_noalloc (FA_BWD_NOALLOC_SCRATCH_BYTES bytes),
+// looked up on the current device's first call and cached per device
+hipError_t bwd_noalloc_scratch(void** ptr);
 
 }  // namespace fa
