@@ -11,8 +11,12 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 
 
 def _lib():
-    from tiled_online_softmax_fa_amd import LIB_PATH, load_library
+    from tiled_online_softmax_fa_amd import LIB_PATH, load_library, open_library
 
+    # the sanitizer run (tests/test_abi_asan.py) points this module at its instrumented build
+    other = os.environ.get("FA_ABI_TEST_LIB")
+    if other:
+        return open_library(other)
     if not os.path.exists(LIB_PATH):
         pytest.skip("libfa.so not built (run __graft_entry__.build())")
     return load_library()

@@ -25,6 +25,7 @@ __all__ = [
     "LIB_PATH",
     "FaError",
     "load_library",
+    "open_library",
     "fwd",
     "fwd_f32",
     "fwd_splitkv",
@@ -73,8 +74,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a library with libfa's C ABI from `path` (not cached; e.g. a checking build) and declare its
+    signatures. Raises if it is missing."""
     if not os.path.exists(path):
-        raise ImportError(f"libfa.so not found at {path}; build it with "
+        raise ImportError(f"{os.path.basename(path)} not found at {path}; build it with "
                           "`python -m tiled_online_softmax_fa_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -103,7 +111,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

@@ -1,6 +1,6 @@
 // C ABI of libfa: argument validation, device check, dispatch to the kernels.
 // Every check that depends only on the arguments runs before any HIP call.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <atomic>
@@ -8,7 +8,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_launch.hpp"
 
 namespace {

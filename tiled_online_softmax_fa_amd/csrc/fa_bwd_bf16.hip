@@ -29,7 +29,7 @@
 //      and dK (details at the kernel).
 #include <mutex>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -126,8 +126,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int G = p.Hq / p.Hkv;
 
   const int n_wg = p.n_tiles * p.B * p.Hkv;  // workgroups per part of the head group
-  const int part = (int)blockIdx.x / n_wg;
-  const TileCoord tc = map_workgroup((int)blockIdx.x - part * n_wg, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
+  const int part = workgroup_index() / n_wg;
+  const TileCoord tc = map_workgroup(workgroup_index() - part * n_wg, p.B * p.Hkv, p.n_tiles, false);  // low key tiles (most work) first
   const int b = tc.head / p.Hkv;
   const int hk = tc.head - b * p.Hkv;
   const int kv0 = tc.tile * BNK;
@@ -401,7 +401,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_dkdv_reduce_kernel(BwdParams p, long long rows) {
   constexpr int LPR = D / 4;  // lanes per row
-  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const long long row = (long long)workgroup_index() * (256 / LPR) + threadIdx.x / LPR;
   const int c4 = threadIdx.x % LPR;
   if (row >= rows) return;
   const int S = p.n_gsplit;
@@ -452,7 +452,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, L = lane & 15;
 
-  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
+  const TileCoord tc = map_workgroup(workgroup_index(), p.B * p.Hq, p.n_tiles, CAUSAL);
   const int b = tc.head / p.Hq;
   const int h = tc.head - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);

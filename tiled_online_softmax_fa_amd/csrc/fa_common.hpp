@@ -64,10 +64,28 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // s_waitcnt encodings for gfx9: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // wait until at most N vector-memory operations of this wave are outstanding
+// (the checking build FA_DEBUG_SYNC waits for all of them: every copy has
+// landed before any tile is read, so no result can depend on copy timing)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+#ifdef FA_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#else
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+#endif
+}
+
+// This workgroup's place in the grid, for the work maps below. The checking
+// build FA_REVERSE_GRID hands the places out in reverse launch order (last
+// first), so that a result depending on which workgroups run first or
+// together would change between the two builds.
+__device__ __forceinline__ int workgroup_index() {
+#ifdef FA_REVERSE_GRID
+  return (int)gridDim.x - 1 - (int)blockIdx.x;
+#else
+  return (int)blockIdx.x;
+#endif
 }
 
 // 16-byte direct global -> LDS copy: lane i writes lds_base + 16 * i.

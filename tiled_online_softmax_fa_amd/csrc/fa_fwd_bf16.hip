@@ -170,8 +170,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   const int L = lane & 15;   // column of an accumulator block (this lane's query)
 
   const int n_wg = p.n_tiles * p.B * p.Hq;  // workgroups per part
-  const int part = SPLIT ? (int)blockIdx.x / n_wg : 0;
-  const TileCoord tc = map_workgroup(SPLIT ? (int)blockIdx.x - part * n_wg : (int)blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
+  const int part = SPLIT ? workgroup_index() / n_wg : 0;
+  const TileCoord tc = map_workgroup(SPLIT ? workgroup_index() - part * n_wg : workgroup_index(), p.B * p.Hq, p.n_tiles, CAUSAL);
   const int b = tc.head / p.Hq;
   const int h = tc.head - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);
@@ -708,7 +708,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void fa_fwd_merge_kernel(FwdParams p, long long rows) {
   constexpr int LPR = D / 4;  // lanes per row
-  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const long long row = (long long)workgroup_index() * (256 / LPR) + threadIdx.x / LPR;
   const int c4 = threadIdx.x % LPR;
   if (row >= rows) return;
   const int S = p.n_splits;

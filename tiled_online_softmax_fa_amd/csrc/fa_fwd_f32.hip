@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_f32_kernel(FwdParams p) {
   const int wave = uniform(tid >> 6);
   const int g = lane >> 4, L = lane & 15;
 
-  const TileCoord tc = map_workgroup(blockIdx.x, p.B * p.Hq, p.n_tiles, CAUSAL);
+  const TileCoord tc = map_workgroup(workgroup_index(), p.B * p.Hq, p.n_tiles, CAUSAL);
   const int b = tc.head / p.Hq;
   const int h = tc.head - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);

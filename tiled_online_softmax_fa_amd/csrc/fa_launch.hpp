@@ -1,7 +1,7 @@
 // Kernel parameter blocks and host-side launchers (C++ linkage, internal to libfa).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 
 namespace fa {

@@ -20,8 +20,8 @@ __global__ __launch_bounds__(256) void fa_quantize_fp8_kernel(const __bf16* __re
                                                               unsigned char* __restrict__ codes,
                                                               float* __restrict__ scale, int N, int n_blk) {
   constexpr int BR = kFp8Block;
-  const int blk = (int)blockIdx.x % n_blk;
-  const size_t head = (size_t)blockIdx.x / n_blk;
+  const int blk = workgroup_index() % n_blk;
+  const size_t head = (size_t)workgroup_index() / n_blk;
   const int r0 = blk * BR;
   const int rows = min(BR, N - r0);
   const size_t base = (head * N + r0) * D;  // first element of the block
