@@ -2,9 +2,12 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): never used by the library.
 
-Both functions walk the keys in blocks, keeping for every query row a running
-maximum m and a running sum l of exponentials, and rescale what was gathered so
-far by exp(m_old - m_new) whenever the maximum grows. They are written from:
+Both functions walk the keys in blocks and, for every query row, carry what the
+blocks seen so far give: the deferred form a running maximum m, a running sum l
+of exponentials and an unnormalised output, rescaled by exp(m_old - m_new)
+whenever the maximum grows; the normalised form the output itself with its
+logsumexp (m + ln l as one number), merged with each block's own normalised
+result. They are written from:
 
 * the page "FlashAttention技术解析：优化Transformer注意力机制" (mhpq.cn),
   section 2.1 (tiled pseudo-code, code operators lost in extraction and
@@ -53,10 +56,25 @@ def _heads(q, k, v):
             yield b, h, q[b, h], k[b, h // G], v[b, h // G]
 
 
-def online_fwd_normalise_each_block(q, k, v, causal, scale, block_q, block_k):
-    """First form: the output is kept normalised after every key block.
+def _block_softmax(q_rows, k_blk, v_blk, scale, causal, row_ids, key_ids):
+    """One key block on its own: its normalised output softmax_blk(s) V_blk and its logsumexp.
 
-    O <- (l / l_new) e^(m - m_new) O + (e^(m_blk - m_new) / l_new) (p_blk V_blk).
+    A row with no visible key in the block gets output 0 and logsumexp -inf.
+    """
+    m_blk, p, l_blk = _block_stats(q_rows, k_blk, scale, causal, row_ids, key_ids)
+    seen = l_blk > 0
+    o_blk = np.where(seen[:, None], (p @ v_blk) / np.where(seen, l_blk, 1.0)[:, None], 0.0)
+    return o_blk, np.where(seen, m_blk + np.log(np.where(seen, l_blk, 1.0)), -np.inf)
+
+
+def online_fwd_normalise_each_block(q, k, v, causal, scale, block_q, block_k):
+    """First form: the running output stays normalised after every key block.
+
+    Written as a merge of normalised partial results. With lse = m + ln l the
+    running maximum and sum of section 2.2 become one number per row, and the
+    update O <- (l / l_new) e^(m - m_new) O + (e^(m_blk - m_new) / l_new) p_blk V_blk
+    is O <- e^(lse - lse_new) O + e^(lse_blk - lse_new) O_blk with
+    lse_new = log(e^lse + e^lse_blk) and O_blk the block's own normalised output.
     Returns (O, lse) like ``attention_fwd``.
     """
     B, Hq, N, d = np.shape(q)
@@ -65,23 +83,18 @@ def online_fwd_normalise_each_block(q, k, v, causal, scale, block_q, block_k):
     for b, h, qh, kh, vh in _heads(q, k, v):
         for i0 in range(0, N, block_q):
             rows = np.arange(i0, min(i0 + block_q, N))
-            q_rows = qh[rows]
-            m = np.full(len(rows), -np.inf)
-            l = np.zeros(len(rows))
-            o = np.zeros((len(rows), d))
+            run_o = np.zeros((len(rows), d))
+            run_lse = np.full(len(rows), -np.inf)
             for j0 in range(0, N, block_k):
                 keys = np.arange(j0, min(j0 + block_k, N))
-                m_blk, p, l_blk = _block_stats(q_rows, kh[keys], scale, causal, rows, keys)
-                m_new = np.maximum(m, m_blk)
-                keep = _safe_exp_diff(m, m_new)
-                gain = _safe_exp_diff(m_blk, m_new)
-                l_new = keep * l + gain * l_blk
-                seen = l_new > 0
-                inv = np.where(seen, 1.0 / np.where(seen, l_new, 1.0), 0.0)
-                o = (l * keep * inv)[:, None] * o + (gain * inv)[:, None] * (p @ vh[keys])
-                m, l = m_new, l_new
-            O[b, h, rows] = o
-            lse[b, h, rows] = m + np.log(l)
+                o_blk, lse_blk = _block_softmax(qh[rows], kh[keys], vh[keys], scale, causal, rows, keys)
+                new_lse = np.logaddexp(run_lse, lse_blk)
+                w_run = _safe_exp_diff(run_lse, new_lse)
+                w_blk = _safe_exp_diff(lse_blk, new_lse)
+                run_o = w_run[:, None] * run_o + w_blk[:, None] * o_blk
+                run_lse = new_lse
+            O[b, h, rows] = run_o
+            lse[b, h, rows] = run_lse
     return O, lse
 
 
