@@ -221,10 +221,21 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   for (int kb = 0; kb < KB; ++kb) lo[kb] = (CAUSAL ? kw0 + kb * 16 + L : 0) - 4 * g;
   const int hi = N - 1 - 4 * g;
 
-  // wave A, query chunk cc of tile j (query rows q0 + 32 cc ..)
+  // wave A, query chunk cc of tile j (query rows q0 + 32 cc ..). Every
+  // fragment a block of matrix instructions needs is read into registers
+  // before the block: the reads of one block are in flight together, and the
+  // dO^T reads of the second product are issued ahead of the exponentials.
   auto chunk_a = [&](const lds_u8* st, int q0, int cc, lds_u8* pb, auto mask) __attribute__((always_inline)) {
     const lds_u8* qt = st;
     const lds_u8* dt = st + QT_BYTES;
+    bf16x8 qa[DC][QB];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) qa[dc][qb] = lds_read_b128(qt + (cc * 32 + qb * 16) * RB + roff(dc));
+    f32x4 l4[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l4[qb] = *(const FA_LDS f32x4*)(st + LSE_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
     f32x4 s[QB][KB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -234,18 +245,22 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bf16x8 a = lds_read_b128(qt + (cc * 32 + qb * 16) * RB + roff(dc));
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], s[qb][kb]);
-      }
+        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = mfma_bf16_16x16x32(qa[dc][qb], kvf[kb][dc], s[qb][kb]);
     __builtin_amdgcn_s_setprio(0);
+    bf16x8 da[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo4 = lds_read_tr16_b64(dt + cc * 32 * RB + toff(db));
+      const i16x4 hi4 = lds_read_tr16_b64(dt + (cc * 32 + 16) * RB + toff(db));
+      da[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
     // P = 2^(c S - lse log2 e); B-operand packing: e < 4 -> query block 0
     // (rows 4g + e), e >= 4 -> block 1 (rows 16 + 4g + e - 4)
     u32x4 pw[KB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const f32x4 l4 = *(const FA_LDS f32x4*)(st + LSE_OFF + (cc * 32 + qb * 16 + 4 * g) * 4);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float e[4];
@@ -256,7 +271,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int qq = q0 + cc * 32 + qb * 16 + r;  // query - 4g
             x = (qq >= lo[kb] && qq <= hi) ? x : kNegInf;
           }
-          e[r] = exp2_fast(fmaf(x, c, -l4[r]));
+          e[r] = exp2_fast(fmaf(x, c, -l4[qb][r]));
         }
         pw[kb][2 * qb] = pack_bf16x2(e[0], e[1]);
         pw[kb][2 * qb + 1] = pack_bf16x2(e[2], e[3]);
@@ -266,20 +281,22 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     for (int kb = 0; kb < KB; ++kb) *(FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024) = pw[kb];
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x4 lo4 = lds_read_tr16_b64(dt + cc * 32 * RB + toff(db));
-      const i16x4 hi4 = lds_read_tr16_b64(dt + (cc * 32 + 16) * RB + toff(db));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, pw[kb]), acc[db][kb]);
-    }
+      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(da[db], __builtin_bit_cast(bf16x8, pw[kb]), acc[db][kb]);
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // wave B, query chunk cc of the previous tile
+  // wave B, query chunk cc of the previous tile (fragments read ahead of
+  // their block, as for wave A)
   auto chunk_b = [&](const lds_u8* st, int cc, const lds_u8* pb) __attribute__((always_inline)) {
     const lds_u8* qt = st;
     const lds_u8* dt = st + QT_BYTES;
+    bf16x8 oa[DC][QB];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oa[dc][qb] = lds_read_b128(dt + (cc * 32 + qb * 16) * RB + roff(dc));
     f32x4 dp[QB][KB];  // dP - D: the accumulators start at -D of their rows
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -287,26 +304,33 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = nd4;
     }
+    u32x4 pr[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) pr[kb] = *(const FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bf16x8 a = lds_read_b128(dt + (cc * 32 + qb * 16) * RB + roff(dc));
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = mfma_bf16_16x16x32(a, kvf[kb][dc], dp[qb][kb]);
-      }
+        for (int kb = 0; kb < KB; ++kb) dp[qb][kb] = mfma_bf16_16x16x32(oa[dc][qb], kvf[kb][dc], dp[qb][kb]);
     __builtin_amdgcn_s_setprio(0);
+    bf16x8 qa[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo4 = lds_read_tr16_b64(qt + cc * 32 * RB + toff(db));
+      const i16x4 hi4 = lds_read_tr16_b64(qt + (cc * 32 + 16) * RB + toff(db));
+      qa[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
     u32x4 dw[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 pw = *(const FA_LDS u32x4*)(pb + (cc * KB + kb) * 1024);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float e[4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const uint32_t w = pw[2 * qb + h2];
+          const uint32_t w = pr[kb][2 * qb + h2];
           const float p0 = __builtin_bit_cast(float, w << 16);
           const float p1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
           e[2 * h2] = p0 * dp[qb][kb][2 * h2];
@@ -318,13 +342,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x4 lo4 = lds_read_tr16_b64(qt + cc * 32 * RB + toff(db));
-      const i16x4 hi4 = lds_read_tr16_b64(qt + (cc * 32 + 16) * RB + toff(db));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, dw[kb]), acc[db][kb]);
-    }
+      for (int kb = 0; kb < KB; ++kb) acc[db][kb] = mfma_bf16_16x16x32(qa[db], __builtin_bit_cast(bf16x8, dw[kb]), acc[db][kb]);
     __builtin_amdgcn_s_setprio(0);
   };
 
