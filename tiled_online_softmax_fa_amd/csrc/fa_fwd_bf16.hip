@@ -319,11 +319,21 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Row sums l. At head dim 64 a chunk has half the matrix work per score
+  // of d = 128 and the vector unit bounds the loop, so there the sums come
+  // from the matrix unit: one more MFMA per query block and chunk, an
+  // all-ones A operand times P^T, leaves in every element of lsum[qb] the
+  // sum of the bf16 probabilities of its query (the same values that weight
+  // V). Elsewhere each lane adds its fp32 probabilities into l_part, and the
+  // four row groups are summed at the end.
+  constexpr bool kRowSumOnMatrix = D == 64;
   float m_ref[QB], l_part[QB];
+  f32x4 lsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = kNegInf;
     l_part[qb] = 0.f;
+    lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c = p.scale_log2;
   // exponent factor of the scores in s_cur (F8: times the Q and K block scales)
@@ -437,7 +447,11 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         const float m_new = fmaxf(m_ref[qb], max_over_row_groups(tmax[qb]));
         const float alpha = (m_ref[qb] == kNegInf) ? 0.f : exp2_fast(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
-        l_part[qb] *= alpha;
+        if constexpr (kRowSumOnMatrix) {
+          lsum[qb] *= alpha;
+        } else {
+          l_part[qb] *= alpha;
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
       }
@@ -457,7 +471,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
       }
       u32x4 packed = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                       pack_bf16x2(e[6], e[7])};
-      l_part[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      if constexpr (!kRowSumOnMatrix) l_part[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       pf[qb] = __builtin_bit_cast(bf16x8, packed);
     }
   };
@@ -467,6 +481,11 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma_bf16_16x16x32(vf[db], pf[qb], acc[db][qb]);
+    if constexpr (kRowSumOnMatrix) {
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lsum[qb] = mfma_bf16_16x16x32(ones, pf[qb], lsum[qb]);
+    }
     if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
@@ -667,7 +686,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
   if constexpr (SPLIT) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float l = sum_over_row_groups(l_part[qb]);
+      const float l = kRowSumOnMatrix ? lsum[qb][0] : sum_over_row_groups(l_part[qb]);
       const int row = qw0 + qb * 16 + L;
       if (row < N) {
         // this part's O (fp32) and lse; a row with no key in the part (l = 0)
@@ -689,7 +708,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     float inv[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float l = sum_over_row_groups(l_part[qb]);
+      const float l = kRowSumOnMatrix ? lsum[qb][0] : sum_over_row_groups(l_part[qb]);
       const int row = qw0 + qb * 16 + L;
       // (sparse: a row that saw no key has l = 0 and gets O = 0, lse = -inf)
       inv[qb] = (!SPARSE || l > 0.f) ? 1.0f / l : 0.f;
