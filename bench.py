@@ -449,15 +449,25 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
 
 def cpu_model():
-    """The host CPU's model name from /proc/cpuinfo (else the machine type)."""
+    """The host CPU's model name from /proc/cpuinfo, with its family and model numbers (else the machine
+    type)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break  # the first processor's block is enough
+                    continue
+                key, val = (x.strip() for x in line.split(":", 1))
+                if key in ("model name", "cpu family", "model") and key not in fields:
+                    fields[key] = val
     except OSError:
         pass
-    return platform.processor() or platform.machine()
+    if "model name" not in fields:
+        return platform.processor() or platform.machine()
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model") if k in fields)
+    return f"{fields['model name']} ({extra})" if extra else fields["model name"]
 
 
 def cpu_baseline(inputs, budget_s=10.0):
